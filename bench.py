@@ -1,0 +1,232 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one exact attention forward on the LLM-prefill workload (B=4,
+Hq=Hkv=32, Nq=Nk=2048, d=128, bf16, causal) followed by one split-KV decode
+(split + combine) on the decode workload (64 sequences, Hq=32, Hkv=8, d=128,
+bf16, L ~ U[512, 32768], 512-key chunks). Inputs are resident in HBM before the
+timed region starts. HIP events on the launch stream bracket every kernel of
+every timed step.
+
+Prints ONE JSON line:
+  value       prefill TFLOP/s = 4*B*H*N*N*d/2 / mean forward kernel time
+  decode      KV GB/s = sum_b 2*Hkv*L_b*d*2 bytes / mean (split + combine) time
+  roofline    the forward kernel against the bf16 dense MFMA peak
+  cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the prefill
+                workload, in the same TFLOP/s unit
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (bf16, d=128, causal) + split-KV decode KV GB/s"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_46_amd", "csrc", f)
+                  for f in ("common.hpp", "attn_fwd.hip", "attn_decode.hip")]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timing (used for profiler runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="restrict the timed step (for per-kernel profiles)")
+    return ap.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """Measured HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+    a copy-kernel calibration), if recorded for the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(w, q, k, v, target_s):
+    """Times the fp64 oracle on a seeded sample of query rows of the prefill workload."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_46_amd import workloads as wl
+
+    qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
+    rng = np.random.default_rng(12345)
+
+    def sample(n):
+        b = rng.integers(0, w.B, n)
+        h = rng.integers(0, w.Hq, n)
+        i = rng.integers(0, w.N, n)
+        return np.stack([b, h, i], axis=1).astype(np.int64)
+
+    def run(rows):
+        t0 = time.perf_counter()
+        oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows)
+        dt = time.perf_counter() - t0
+        flops = float(np.sum(4.0 * (rows[:, 2] + 1) * w.d))  # metric convention, causal
+        return dt, flops
+
+    dt, fl = run(sample(256))
+    n = int(min(2_000_000, max(256, 256 * target_s / max(dt, 1e-3))))
+    rows = sample(n)
+    dt, fl = run(rows)
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d seeded random query rows of the llm_prefill workload (exact fp64 "
+                      "causal rows, avg %d keys), %.1f s" % (n, int(rows[:, 2].mean()) + 1, dt),
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_attention_46_amd as ea
+    from exact_attention_46_amd import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ea.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wp = wl.WORKLOADS["llm_prefill"]
+    wd = wl.WORKLOADS["decode"]
+    do_pre = args.only in ("all", "prefill")
+    do_dec = args.only in ("all", "decode")
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    q, k, v = wl.workload_prefill_inputs(wp)
+    qg, kg, vg = q.to(dev), k.to(dev), v.to(dev)
+    og = torch.empty_like(qg)
+    lseg = torch.empty((wp.B, wp.Hq, wp.N), dtype=torch.float32, device=dev)
+
+    sl, dq, kc, vc = (None,) * 4
+    if do_dec:
+        sl, dq, kc, vc = wl.workload_decode_inputs(wd, device=dev)
+        dq, sld = dq.to(dev), sl.to(dev)
+        bufs = ea.decode_buffers(dq, wd.l_max, wd.chunk)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if do_pre:
+            ea.attn_fwd(qg, kg, vg, og, lseg, True, wp.scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if do_dec:
+            ea.attn_decode_split(dq, kc, vc, sld, bufs[0], bufs[1], wd.chunk, wd.scale, stream)
+            if ev is not None:
+                ev[2].record(stream)
+            ea.attn_decode_combine(bufs[0], bufs[1], sld, bufs[2], bufs[3], wd.chunk, stream)
+        elif ev is not None:
+            ev[2].record(stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print("bench: timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
+
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    split_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    comb_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in events]))
+
+    flops = 4.0 * wp.B * wp.Hq * wp.N * wp.N * wp.d / 2.0
+    tflops = flops / (fwd_ms * 1e-3) / 1e12 if do_pre else None
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2) if tflops else None,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn inputs, no dataset)",
+        "config": {"workload": "llm_prefill: B=4 Hq=Hkv=32 Nq=Nk=2048 d=128 bf16 causal, "
+                               "then decode: 64 seqs Hq=32 Hkv=8 d=128 bf16 "
+                               "L~U[512,32768] chunk=512",
+                   "fwd_ms": round(fwd_ms, 4)},
+    }
+    if do_pre:
+        traffic = load_traffic("attn_fwd_kernel/llm_prefill")
+        out["roofline"] = {"kernel": "attn_fwd_kernel<bf16,128,causal>", "bound": "mfma",
+                           "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic,
+                           "algorithmic_bytes": 4 * wp.B * wp.Hq * wp.N * wp.d * 2
+                           + wp.B * wp.Hq * wp.N * 4}
+    if do_dec:
+        lens = sl.numpy().astype(np.int64)
+        kv_bytes = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
+        dec_ms = split_ms + comb_ms
+        gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+        out["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "split_ms": round(split_ms, 4),
+                         "combine_ms": round(comb_ms, 4),
+                         "split_only_GBs": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1),
+                         "kv_bytes": int(kv_bytes),
+                         "roofline": {"kernel": "attn_decode_split_kernel<bf16,128>",
+                                      "bound": "hbm", "achieved": round(gbs, 1),
+                                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                      "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                      "traffic": load_traffic("attn_decode_split_kernel/decode")}}
+    if not args.no_cpu_baseline and do_pre:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wp, q, k, v, args.cpu_seconds)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""MI355X-native exact attention: fused forward with LSE and split-KV decode.
+
+The compute runs in hand-written HIP kernels for gfx950 behind a C ABI
+(``include/mi355attn.h``, built into ``libmi355attn.so``); this package is the
+thin Python binding over it. The library is loaded on first use and there is
+no CPU fallback.
+"""
+from ._binding import (  # noqa: F401
+    AttnError,
+    EXPORTS,
+    LIB_PATH,
+    attn_decode_combine,
+    attn_decode_split,
+    attn_fwd,
+    attn_status_str,
+    decode,
+    decode_buffers,
+    default_scale,
+    fwd,
+    load_library,
+)

@@ -1,0 +1,183 @@
+"""ctypes binding of ``libmi355attn.so``: argument marshalling only.
+
+The functions with the C names (``attn_fwd``, ``attn_decode_split``,
+``attn_decode_combine``, ``attn_status_str``) take torch tensors that already
+live on the GPU, check that they match the C contract (device, dtype,
+contiguity, shapes), pass their device pointers and torch's current HIP stream,
+and raise ``AttnError`` on a non-zero status. ``fwd`` and ``decode`` also
+allocate the outputs. Every step of the computation runs in the HIP kernels;
+nothing here computes attention, and there is no CPU fallback: if the library
+is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmi355attn.so")
+
+OK = 0
+ERR_NULL_PTR = -1
+ERR_BAD_SHAPE = -2
+ERR_UNSUPPORTED = -3
+ERR_MISALIGNED = -4
+ERR_BAD_ARG = -5
+ERR_HIP = -6
+
+EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_combine", "attn_status_str")
+
+_DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed with status %d: %s" % (fn, status, attn_status_str(status)))
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Loads the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libmi355attn.so is not built (run python -m "
+                               "exact_attention_46_amd.build); there is no fallback")
+        lib = ctypes.CDLL(LIB_PATH)
+        p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
+        lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
+        lib.attn_decode_combine.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p]
+        lib.attn_status_str.argtypes = [i]
+        lib.attn_fwd.restype = i
+        lib.attn_decode_split.restype = i
+        lib.attn_decode_combine.restype = i
+        lib.attn_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def attn_status_str(status: int) -> str:
+    return load_library().attn_status_str(int(status)).decode()
+
+
+def _ptr(t: torch.Tensor):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _gpu(*ts):
+    for t in ts:
+        _need(t.is_cuda, "tensors must be on the GPU (no CPU path exists)")
+        _need(t.is_contiguous(), "tensors must be contiguous")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    _need(t.dtype in _DTYPE_CODE, "q/k/v must be bfloat16 or float16")
+    return _DTYPE_CODE[t.dtype]
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """Calls attn_fwd. q/o [B,Hq,Nq,d], k/v [B,Hkv,Nk,d], lse [B,Hq,Nq] fp32."""
+    _gpu(q, k, v, o, lse)
+    _need(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D, k ~ v")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape[0] == B and k.shape[3] == d, "k/v batch or head dim differ from q")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype and o.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape, "o must have q's shape")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq, Nq), "lse [B,Hq,Nq] fp32")
+    st = load_library().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq,
+                                 Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                 _stream(stream))
+    if st != OK:
+        raise AttnError("attn_fwd", st)
+
+
+def attn_decode_split(q, k_cache, v_cache, seq_lens, part_o, part_lse, chunk: int,
+                      scale: float, stream=None) -> None:
+    """Calls attn_decode_split. q [B,Hq,d], caches [B,Hkv,max_len,d], seq_lens [B] int32,
+    part_o [B,Hq,C,d] fp32, part_lse [B,Hq,C] fp32 with C = ceil(max_len/chunk)."""
+    _gpu(q, k_cache, v_cache, seq_lens, part_o, part_lse)
+    B, Hq, d = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    _need(v_cache.shape == k_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d,
+          "cache shapes")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype, "dtypes differ")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens [B] int32")
+    C = -(-max_len // chunk)
+    _need(part_o.dtype == torch.float32 and tuple(part_o.shape) == (B, Hq, C, d), "part_o shape")
+    _need(part_lse.dtype == torch.float32 and tuple(part_lse.shape) == (B, Hq, C),
+          "part_lse shape")
+    st = load_library().attn_decode_split(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                          _ptr(part_o), _ptr(part_lse), B, Hq, Hkv, max_len, d,
+                                          int(chunk), float(scale), _dtype_code(q),
+                                          _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode_split", st)
+
+
+def attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk: int, stream=None) -> None:
+    """Calls attn_decode_combine. o [B,Hq,d] bf16/fp16, lse [B,Hq] fp32."""
+    _gpu(part_o, part_lse, seq_lens, o, lse)
+    B, Hq, C, d = part_o.shape
+    _need(o.dtype in _DTYPE_CODE and tuple(o.shape) == (B, Hq, d), "o [B,Hq,d] bf16/fp16")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq), "lse [B,Hq] fp32")
+    _need(tuple(part_lse.shape) == (B, Hq, C), "part_lse shape")
+    st = load_library().attn_decode_combine(_ptr(part_o), _ptr(part_lse), _ptr(seq_lens),
+                                            _ptr(o), _ptr(lse), B, Hq, C, d, int(chunk),
+                                            _DTYPE_CODE[o.dtype], _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode_combine", st)
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
+    """Allocates and returns (o, lse) for attention forward."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def decode_buffers(q, max_len: int, chunk: int):
+    """Allocates (part_o, part_lse, o, lse) for a decode of q [B,Hq,d]."""
+    B, Hq, d = q.shape
+    C = -(-max_len // chunk)
+    part_o = torch.empty((B, Hq, C, d), dtype=torch.float32, device=q.device)
+    part_lse = torch.empty((B, Hq, C), dtype=torch.float32, device=q.device)
+    o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    return part_o, part_lse, o, lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, chunk: int = 512, scale: float | None = None,
+           stream=None, buffers=None):
+    """Split-KV decode: split then combine on the same stream. Returns (o, lse)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    if buffers is None:
+        buffers = decode_buffers(q, k_cache.shape[2], chunk)
+    part_o, part_lse, o, lse = buffers
+    attn_decode_split(q, k_cache, v_cache, seq_lens, part_o, part_lse, chunk, scale, stream)
+    attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk, stream)
+    return o, lse

@@ -1,0 +1,84 @@
+// C ABI of the attention library: argument checks, then one launch per call.
+// Every check runs before any HIP call, so a rejected call has no side effect.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/mi355attn.h"
+#include "launch.hpp"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool dtype_ok(int dt) { return dt == MI355ATTN_BF16 || dt == MI355ATTN_FP16; }
+bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MI355ATTN_OK : MI355ATTN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                        int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::fwd_grid_blocks(B, Hq, Nq) > kMaxGrid || (int64_t)B * Hq > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype};
+  return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seq_lens, float* part_o, float* part_lse, int B,
+                                 int Hq, int Hkv, int max_len, int d, int chunk, float scale,
+                                 int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !part_o || !part_lse)
+    return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0 || chunk <= 0)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype) || Hq / Hkv > 32) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16) ||
+      !aligned(part_lse, 4) || !aligned(seq_lens, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::split_grid_blocks(B, Hkv, max_len, chunk) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::SplitArgs a{q, k_cache, v_cache, seq_lens, part_o, part_lse, B, Hq, Hkv, max_len,
+                         d, chunk, scale, dtype};
+  return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int attn_decode_combine(const float* part_o, const float* part_lse,
+                                   const int* seq_lens, void* o, float* lse, int B, int Hq,
+                                   int max_chunks, int d, int chunk, int dtype, void* stream) {
+  if (!part_o || !part_lse || !seq_lens || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || max_chunks <= 0 || d <= 0 || chunk <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(seq_lens, 4) || !aligned(o, 16) ||
+      !aligned(lse, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (((int64_t)B * Hq + 3) / 4 > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::CombineArgs a{part_o, part_lse, seq_lens, o, lse, B, Hq, max_chunks, d, chunk, dtype};
+  return from_hip(mi355attn::launch_combine(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" const char* attn_status_str(int status) {
+  switch (status) {
+    case MI355ATTN_OK: return "ok";
+    case MI355ATTN_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MI355ATTN_ERR_BAD_SHAPE: return "bad shape: a size <= 0, Hq % Hkv != 0, or grid too large";
+    case MI355ATTN_ERR_UNSUPPORTED: return "unsupported: head dim, dtype or Hq/Hkv not supported";
+    case MI355ATTN_ERR_MISALIGNED: return "misaligned pointer (16 bytes for tensors, 4 for lse/lens)";
+    case MI355ATTN_ERR_BAD_ARG: return "bad argument: scale must be finite and > 0, causal 0 or 1";
+    case MI355ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}

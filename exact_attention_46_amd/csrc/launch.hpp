@@ -1,0 +1,51 @@
+// Host-side launch descriptors shared by the C ABI and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi355attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int dtype;
+};
+
+struct SplitArgs {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int* seq_lens;
+  float* part_o;
+  float* part_lse;
+  int B, Hq, Hkv, max_len, d, chunk;
+  float scale;
+  int dtype;
+};
+
+struct CombineArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int* seq_lens;
+  void* o;
+  float* lse;
+  int B, Hq, max_chunks, d, chunk;
+  int dtype;
+};
+
+// Number of workgroups the forward launch uses (for the grid-size check).
+int64_t fwd_grid_blocks(int B, int Hq, int Nq);
+int64_t split_grid_blocks(int B, int Hkv, int max_len, int chunk);
+
+hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace mi355attn

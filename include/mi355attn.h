@@ -1,0 +1,128 @@
+/*
+ * mi355attn — exact fused attention forward and split-KV decode for MI355X
+ * (gfx950 / CDNA4). C ABI.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense, row-major, in device memory owned by the caller. The
+ *    library allocates nothing, keeps no workspace and no mutable global state,
+ *    and may be called from several host threads at once.
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *    Every call only enqueues work on that stream and returns at once.
+ *  - The return value covers argument checks and the launch itself
+ *    (hipGetLastError after the launch), never the completion of the kernels.
+ *    Argument checks run before any HIP call, so a rejected call touches no GPU
+ *    state. No call aborts or throws.
+ *  - `dtype` selects the 16-bit element type of q, k, v and o:
+ *    MI355ATTN_BF16 (0) or MI355ATTN_FP16 (1). LSE values are always fp32.
+ *  - q, k, v, o, the caches and part_o must be 16-byte aligned (the kernels use
+ *    128-bit loads and stores); lse, part_lse and seq_lens 4-byte aligned.
+ *  - Offsets are computed in 64 bits; a single tensor may exceed 2^31 elements.
+ *  - `scale` multiplies q.k before the mask and the exponential; it must be
+ *    finite and > 0 (the usual value is 1/sqrt(d)).
+ *  - The LSE is the natural log of sum_j exp(scale * q.k_j) over the allowed keys
+ *    (as in the rustytorch "flash_attention_forward.cu" page,
+ *    OnlineSoftmaxState::get_log_sum_exp). A row with no allowed key gets O = 0
+ *    and LSE = -inf.
+ */
+#ifndef MI355ATTN_H
+#define MI355ATTN_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type codes. */
+#define MI355ATTN_BF16 0
+#define MI355ATTN_FP16 1
+
+/* Status codes. */
+#define MI355ATTN_OK 0
+#define MI355ATTN_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
+#define MI355ATTN_ERR_BAD_SHAPE (-2)   /* a size <= 0, Hq % Hkv != 0, or a grid too large */
+#define MI355ATTN_ERR_UNSUPPORTED (-3) /* d not in {64, 128}, unknown dtype, Hq/Hkv > 32 in decode */
+#define MI355ATTN_ERR_MISALIGNED (-4)  /* a pointer breaks the alignment rule above */
+#define MI355ATTN_ERR_BAD_ARG (-5)     /* scale not finite or <= 0, causal not 0/1 */
+#define MI355ATTN_ERR_HIP (-6)         /* the HIP runtime reported an error at launch */
+
+/*
+ * attn_fwd — exact attention forward with per-row log-sum-exp.
+ *
+ *   O = softmax(scale * Q K^T + mask) V,   LSE_i = log sum_j exp(scale * q_i.k_j)
+ *
+ * computed tile by tile with the online-softmax rescale, so the Nq x Nk score
+ * matrix never exists in memory (the algorithm described in the module
+ * documentation of the abaddon "attention.rs" page: Q tile resident, K/V tiles
+ * streamed, running max and sum, final division by the sum).
+ *
+ *   q   [B, Hq,  Nq, d]   dtype        (read)
+ *   k   [B, Hkv, Nk, d]   dtype        (read)
+ *   v   [B, Hkv, Nk, d]   dtype        (read)
+ *   o   [B, Hq,  Nq, d]   dtype        (written, rounded to nearest even)
+ *   lse [B, Hq,  Nq]      float        (written)
+ *
+ * Query head h reads key/value head floor(h * Hkv / Hq) (grouped-query
+ * attention, as in the abaddon page's flash_attention_f16); Hq must be a
+ * multiple of Hkv. d must be 64 or 128. causal = 1 allows key j for query row i
+ * iff j <= i + (Nk - Nq) (aligned to the bottom-right corner; for Nq == Nk this
+ * is the pages' j <= i); causal = 0 allows every key.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_decode_split — first half of split-KV ("flash decoding") decode: one new
+ * query token per sequence against a padded KV cache, split into chunks of
+ * `chunk` keys; each chunk emits its own normalised partial output and LSE
+ * (the partials that the aprender-gpu "flash_decoding/reduce_kernel.rs" page's
+ * reduction consumes, stored here as O_c and LSE_c = m_c + log l_c instead of
+ * the unnormalised sum with separate max and sum; the two carry the same
+ * information).
+ *
+ *   q        [B, Hq, d]                dtype  (read)
+ *   k_cache  [B, Hkv, max_len, d]      dtype  (read: rows < seq_lens[b] only)
+ *   v_cache  [B, Hkv, max_len, d]      dtype  (read: rows < seq_lens[b] only)
+ *   seq_lens [B]                       int32, device memory (read); values are
+ *                                      clamped to [0, max_len]
+ *   part_o   [B, Hq, C, d]             float  (written for chunks c < ceil(L_b/chunk))
+ *   part_lse [B, Hq, C]                float  (written for every c; -inf past the end)
+ *
+ * with C = ceil(max_len / chunk). Chunk c of sequence b covers keys
+ * [c*chunk, min((c+1)*chunk, L_b)). d must be 64 or 128 and Hq/Hkv <= 32.
+ */
+int attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, float* part_o, float* part_lse, int B, int Hq,
+                      int Hkv, int max_len, int d, int chunk, float scale, int dtype,
+                      void* stream);
+
+/*
+ * attn_decode_combine — second half of split-KV decode: merges the partials of
+ * each (b, h) with the rescaling combine (the two passes of the aprender-gpu
+ * reduce kernel: global maximum M of the chunk LSEs, then weights
+ * exp(LSE_c - M), weighted mean of the chunk outputs):
+ *
+ *   O = sum_c w_c O_c / sum_c w_c,   LSE = M + log(sum_c w_c)
+ *
+ * over the first ceil(L_b / chunk) chunks (capped at max_chunks); chunks whose
+ * LSE is -inf carry no weight.
+ *
+ *   part_o   [B, Hq, max_chunks, d]  float  (read)
+ *   part_lse [B, Hq, max_chunks]     float  (read)
+ *   seq_lens [B]                     int32, device memory (read, clamped at 0)
+ *   o        [B, Hq, d]              dtype  (written, rounded to nearest even)
+ *   lse      [B, Hq]                 float  (written)
+ *
+ * max_chunks and chunk must be the C and chunk used for attn_decode_split.
+ */
+int attn_decode_combine(const float* part_o, const float* part_lse, const int* seq_lens,
+                        void* o, float* lse, int B, int Hq, int max_chunks, int d, int chunk,
+                        int dtype, void* stream);
+
+/* A static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MI355ATTN_H */

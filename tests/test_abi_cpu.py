@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status codes
+before making any HIP call (only invalid calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_46_amd as ea
+from exact_attention_46_amd import build as ea_build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "mi355attn.h")
+
+A = ctypes.c_void_p(4096)   # aligned, non-NULL stand-ins: never dereferenced,
+A2 = ctypes.c_void_p(8192)  # every call below fails validation first
+MIS = ctypes.c_void_p(4098)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+
+
+def header_defines():
+    out = {}
+    for name, val in re.findall(r"#define\s+(MI355ATTN_\w+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
+        out[name] = int(val)
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ea.load_library()
+
+
+def test_library_built_for_gfx950():
+    assert ea_build.ARCH == "gfx950"
+    assert os.path.exists(ea.LIB_PATH)
+
+
+def test_every_declared_function_is_exported(lib):
+    names = declared_functions()
+    assert sorted(names) == sorted(ea.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_codes_match_header(lib):
+    d = header_defines()
+    assert d["MI355ATTN_OK"] == ea._binding.OK
+    assert d["MI355ATTN_ERR_NULL_PTR"] == ea._binding.ERR_NULL_PTR
+    assert d["MI355ATTN_ERR_BAD_SHAPE"] == ea._binding.ERR_BAD_SHAPE
+    assert d["MI355ATTN_ERR_UNSUPPORTED"] == ea._binding.ERR_UNSUPPORTED
+    assert d["MI355ATTN_ERR_MISALIGNED"] == ea._binding.ERR_MISALIGNED
+    assert d["MI355ATTN_ERR_BAD_ARG"] == ea._binding.ERR_BAD_ARG
+    assert d["MI355ATTN_ERR_HIP"] == ea._binding.ERR_HIP
+    assert d["MI355ATTN_BF16"] == 0 and d["MI355ATTN_FP16"] == 1
+    for code in range(-6, 1):
+        s = ea.attn_status_str(code)
+        assert s and s != "unknown status"
+    assert ea.attn_status_str(123) == "unknown status"
+
+
+def fwd(lib, q=A, k=A, v=A, o=A2, lse=A2, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, d=128, scale=0.1,
+        causal=1, dtype=0):
+    return lib.attn_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Nq=0), -2), (dict(Nk=-1), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(B=2**30, Hq=2**10, Nq=128 * 4), -2),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=2), -3),
+    (dict(scale=0.0), -5), (dict(scale=-1.0), -5), (dict(scale=float("nan")), -5),
+    (dict(scale=float("inf")), -5), (dict(causal=2), -5),
+    (dict(q=MIS), -4), (dict(o=MIS), -4), (dict(lse=ctypes.c_void_p(4097)), -4),
+])
+def test_attn_fwd_rejects(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def split(lib, q=A, kc=A, vc=A, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2, max_len=64, d=128,
+          chunk=16, scale=0.1, dtype=0):
+    return lib.attn_decode_split(q, kc, vc, sl, po, pl, B, Hq, Hkv, max_len, d, chunk, scale,
+                                 dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kc=None), -1), (dict(sl=None), -1), (dict(po=None), -1),
+    (dict(B=0), -2), (dict(max_len=0), -2), (dict(chunk=0), -2), (dict(Hq=6, Hkv=4), -2),
+    (dict(d=80), -3), (dict(dtype=5), -3), (dict(Hq=66, Hkv=2), -3),
+    (dict(scale=0.0), -5), (dict(kc=MIS), -4), (dict(sl=ctypes.c_void_p(4098)), -4),
+    (dict(B=2**20, Hkv=2**10, max_len=2**20, chunk=1), -2),
+])
+def test_attn_decode_split_rejects(lib, kw, code):
+    assert split(lib, **kw) == code
+
+
+def combine(lib, po=A, pl=A2, sl=A2, o=A, lse=A2, B=2, Hq=8, C=4, d=128, chunk=16, dtype=0):
+    return lib.attn_decode_combine(po, pl, sl, o, lse, B, Hq, C, d, chunk, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(po=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(C=0), -2), (dict(chunk=-3), -2),
+    (dict(d=32), -3), (dict(dtype=-1), -3), (dict(po=MIS), -4), (dict(o=MIS), -4),
+])
+def test_attn_decode_combine_rejects(lib, kw, code):
+    assert combine(lib, **kw) == code
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        ea.fwd(q, q, q)
