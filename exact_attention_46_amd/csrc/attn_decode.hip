@@ -36,8 +36,8 @@ struct SplitLayout {
   static constexpr int kWaveBytes = kKBytes + kVBytes;
   static constexpr int kLds = kSplitWaves * kWaveBytes;
   // The merge of the 4 waves reuses the same LDS: per wave 32 columns x D
-  // floats of O plus 32 (m, l) pairs.
-  static constexpr int kMergeBytes = kSplitWaves * (32 * D + 64) * 4;
+  // floats of O plus 32 (m, l, l_rounded, pad) quadruples.
+  static constexpr int kMergeBytes = kSplitWaves * (32 * D + 128) * 4;
   static_assert(kMergeBytes <= kLds, "merge area must fit in the staging LDS");
 };
 
@@ -147,7 +147,8 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   const float cl = scale * kLog2e;
   float m_used = -INFINITY;
-  float l_part = 0.f;
+  float l_part = 0.f;   // row sum of the unrounded P (for the LSE)
+  float lr_part = 0.f;  // row sum of the rounded P fed to the MFMA (normalises O)
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
@@ -186,6 +187,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
         m_used = m_new;
         l_part *= alpha;
+        lr_part *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -206,6 +208,12 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         pf[j] = (u32x4_t){pack2<DT>(p[8 * j + 0], p[8 * j + 1]), pack2<DT>(p[8 * j + 2], p[8 * j + 3]),
                           pack2<DT>(p[8 * j + 4], p[8 * j + 5]), pack2<DT>(p[8 * j + 6], p[8 * j + 7])};
       }
+      float lrsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
+      lr_part += lrsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const unsigned char* vrow = vt + (db * 32 + r32) * Lay::kVPitch + half * 16;
@@ -218,11 +226,14 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     }
   }
 
-  // ---- merge the 4 waves: each publishes (m, l) and its unnormalised O^T.
+  // ---- merge the 4 waves: each publishes (m, l, l_rounded) and its
+  // unnormalised O^T; O_c = sum_w a_w O_w / sum_w a_w lr_w and
+  // LSE_c = ln2 * (M + log2 sum_w a_w l_w) with a_w = 2^(m_w - M).
   const float l_row = sum_with_partner32(l_part);
+  const float lr_row = sum_with_partner32(lr_part);
   __syncthreads();  // all waves are done with the staging LDS
   float* mo = reinterpret_cast<float*>(smem);                  // [wave][32][D]
-  float* ml = mo + kSplitWaves * 32 * D;                        // [wave][32][2]
+  float* ml = mo + kSplitWaves * 32 * D;                        // [wave][32][4]
   if (r32 < R) {
     float* dst = mo + ((int64_t)wave * 32 + r32) * D;
 #pragma unroll
@@ -230,8 +241,9 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
       for (int e = 0; e < 16; ++e) dst[db * 32 + 8 * (e >> 2) + 4 * half + (e & 3)] = oacc[db][e];
     if (half == 0) {
-      ml[(wave * 32 + r32) * 2 + 0] = m_used;
-      ml[(wave * 32 + r32) * 2 + 1] = l_row;
+      ml[(wave * 32 + r32) * 4 + 0] = m_used;
+      ml[(wave * 32 + r32) * 4 + 1] = l_row;
+      ml[(wave * 32 + r32) * 4 + 2] = lr_row;
     }
   }
   __syncthreads();
@@ -239,17 +251,18 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int r = idx / D, dd = idx % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, ml[(w * 32 + r) * 2]);
-    float num = 0.f, den = 0.f;
+    for (int w = 0; w < kSplitWaves; ++w) M = fmaxf(M, ml[(w * 32 + r) * 4]);
+    float num = 0.f, den = 0.f, den_r = 0.f;
 #pragma unroll
     for (int w = 0; w < kSplitWaves; ++w) {
-      const float mw = ml[(w * 32 + r) * 2];
+      const float mw = ml[(w * 32 + r) * 4];
       const float wt = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-      den += wt * ml[(w * 32 + r) * 2 + 1];
+      den += wt * ml[(w * 32 + r) * 4 + 1];
+      den_r += wt * ml[(w * 32 + r) * 4 + 2];
       num += wt * mo[((int64_t)w * 32 + r) * D + dd];
     }
     const int64_t row = (int64_t)b * Hq + (int64_t)g * R + r;
-    part_o[(row * C + c) * D + dd] = den > 0.f ? num / den : 0.f;
+    part_o[(row * C + c) * D + dd] = den > 0.f ? num / den_r : 0.f;
     if (dd == 0) part_lse[row * C + c] = den > 0.f ? kLn2 * (M + fast_log2(den)) : -INFINITY;
   }
 }

@@ -23,6 +23,11 @@
 // the row maximum grows by more than kTau (log2 units), so P <= 2^kTau and O is
 // rescaled rarely. The result is the same quantity: O = sum 2^(u-m) v / sum
 // 2^(u-m) for any fixed m, and LSE = ln2 * (m + log2 sum 2^(u-m)).
+//
+// Two row sums are kept: the sum of the unrounded fp32 P (for the LSE) and the
+// sum of the 16-bit P values that actually enter the P V product (to normalise
+// O). With the latter the weights applied to V sum to exactly one, so the
+// rounding of a dominant P cancels instead of scaling its V row.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -181,7 +186,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // ---- per-row state (identical in lanes l and l ^ 32)
   const float c = scale * kLog2e;
   float m_used = -INFINITY;  // exponent offset, log2 units
-  float l_part = 0.f;        // this lane's share of the row sum
+  float l_part = 0.f;        // this lane's share of the row sum (unrounded P)
+  float lr_part = 0.f;       // the same over the rounded P fed to the MFMA
   f32x16_t oacc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
@@ -250,6 +256,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
         m_used = m_new;
         l_part *= alpha;
+        lr_part *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -277,6 +284,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         }
       }
       l_part += lsum;
+      float lrsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
+      lr_part += lrsum;
 
       // O^T += V^T * P^T: 16-key steps; lane-half `half` reads the 8 keys
       // 16*ks + {8*(m/4) + 4*half + m%4}, stored contiguously at 16*ks + 8*half.
@@ -297,9 +310,10 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
   const float l_row = sum_with_partner32(l_part);
+  const float lr_row = sum_with_partner32(lr_part);
   if (my_row < Nq) {
     const bool empty = !(l_row > 0.f);
-    const float inv = empty ? 0.f : 1.f / l_row;
+    const float inv = empty ? 0.f : 1.f / lr_row;
     uint16_t* orow = o + (((int64_t)b * Hq + h) * (int64_t)Nq + my_row) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {

@@ -68,6 +68,18 @@ __device__ __forceinline__ uint32_t hi_halves(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// acc + lo + hi of a dword holding two 16-bit values (exact products with 1.0).
+template <int DT>
+__device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
+                                           __builtin_bit_cast(bf16x2_t, 0x3f803f80u), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed),
+                                  __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
