@@ -15,6 +15,9 @@ bool dtype_ok(int dt) { return dt == MI355ATTN_BF16 || dt == MI355ATTN_FP16; }
 bool scale_ok(float s) { return isfinite(s) && s > 0.f; }
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
+// Longest sequence: keeps the kernels' 32-bit per-head byte offsets and row
+// index arithmetic exact (2^23 rows x 256 bytes = 2 GiB per head).
+constexpr int kMaxSeq = 1 << 23;
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MI355ATTN_OK : MI355ATTN_ERR_HIP; }
 
@@ -25,7 +28,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
                         int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
-  if (Hq % Hkv != 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || Nq > kMaxSeq || Nk > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
   if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
   if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
@@ -44,7 +47,7 @@ extern "C" int attn_decode_split(const void* q, const void* k_cache, const void*
     return MI355ATTN_ERR_NULL_PTR;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0 || chunk <= 0)
     return MI355ATTN_ERR_BAD_SHAPE;
-  if (Hq % Hkv != 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || max_len > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
   if (!head_dim_ok(d) || !dtype_ok(dtype) || Hq / Hkv > 32) return MI355ATTN_ERR_UNSUPPORTED;
   if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16) ||

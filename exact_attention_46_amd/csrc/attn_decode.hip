@@ -41,9 +41,21 @@ struct SplitLayout {
   static_assert(kMergeBytes <= kLds, "merge area must fit in the staging LDS");
 };
 
+// Key position inside the 32-key V^T tile row: bits 2 and 3 of the offset in
+// each 16-key group swapped, so the 8 keys one MFMA lane-half consumes per
+// 16-key step are contiguous.
 __device__ __forceinline__ int vt_pos32(int key) {
   int o = key & 15;
   return (key & ~15) | ((o & 4) << 1) | ((o & 8) >> 1) | (o & 3);
+}
+
+// Byte offset of (row d, key position pos) in the V^T tile; the 16-byte slot
+// index is XOR-ed with (d >> 3) & 3 so that the staging writes of rows
+// d = 8c + e (one slot, many c) spread over the LDS banks.
+template <int PITCH>
+__device__ __forceinline__ int vt_off32(int d, int pos) {
+  const int slot = (pos >> 3) ^ ((d >> 3) & 3);
+  return d * PITCH + slot * 16 + (pos & 7) * 2;
 }
 
 template <int DT, int D>
@@ -83,8 +95,12 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int n_tiles = (n_keys + kSplitBN - 1) / kSplitBN;
   const int iters = (n_tiles + kSplitWaves - 1) / kSplitWaves;
 
+  // Buffer resources cover only the L valid rows of this (b, g): cache rows
+  // past the end of the sequence read as zero and are never fetched.
   const uint16_t* kg = kc + ((int64_t)b * Hkv + g) * (int64_t)max_len * D;
   const uint16_t* vg = vc + ((int64_t)b * Hkv + g) * (int64_t)max_len * D;
+  const auto rk = make_rsrc(kg, (uint32_t)L * (D * 2));
+  const auto rv = make_rsrc(vg, (uint32_t)L * (D * 2));
 
   // Q^T operand: column r32 is query head g*R + r32 (zero for r32 >= R).
   u32x4_t qf[DS];
@@ -107,17 +123,15 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   unsigned char* kt = smem + wave * Lay::kWaveBytes;
   unsigned char* vt = kt + Lay::kKBytes;
 
+  const uint32_t st_off = (uint32_t)(st_a * KPL) * (D * 2) + st_c * 16;
   auto gload = [&](int tile) {
+    // Rows at or past the chunk end belong to the next chunk (or lie past L):
+    // they are loaded but masked out of the scores; the values are finite.
+    const uint32_t base = (uint32_t)(lo + (int64_t)tile * kSplitBN) * (D * 2) + st_off;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
-      const int64_t key = lo + (int64_t)tile * kSplitBN + st_a * KPL + i;
-      if (tile < n_tiles && key < hi) {
-        kreg[i] = *reinterpret_cast<const u32x4_t*>(kg + key * D + st_c * 8);
-        vreg[i] = *reinterpret_cast<const u32x4_t*>(vg + key * D + st_c * 8);
-      } else {
-        kreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-        vreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
+      kreg[i] = buf_load16(rk, base + i * (D * 2));
+      vreg[i] = buf_load16(rv, base + i * (D * 2));
     }
   };
 
@@ -128,7 +142,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // V^T: for each d of the chunk, groups of 4 consecutive keys side by side.
 #pragma unroll
     for (int g4 = 0; g4 < KPL / 4; ++g4) {
-      unsigned char* dst = vt + vt_pos32(st_a * KPL + 4 * g4) * 2;
+      const int pos = vt_pos32(st_a * KPL + 4 * g4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
@@ -140,7 +154,8 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           w0 = lo_halves(vreg[4 * g4 + 0][w], vreg[4 * g4 + 1][w]);
           w1 = lo_halves(vreg[4 * g4 + 2][w], vreg[4 * g4 + 3][w]);
         }
-        *reinterpret_cast<u32x2_t*>(dst + (st_c * 8 + e) * Lay::kVPitch) = (u32x2_t){w0, w1};
+        *reinterpret_cast<u32x2_t*>(vt + vt_off32<Lay::kVPitch>(st_c * 8 + e, pos)) =
+            (u32x2_t){w0, w1};
       }
     }
   };
@@ -159,7 +174,9 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     __syncthreads();  // previous readers of this wave's LDS are done
     lds_store();
     __syncthreads();
-    if (it + 1 < iters) gload(tile + kSplitWaves);
+    // Unconditional prefetch (the last iteration re-reads its own tile) keeps
+    // every buffer load provably complete at the store above.
+    gload(it + 1 < iters ? tile + kSplitWaves : tile);
     if (tile < n_tiles) {
       f32x16_t s = (f32x16_t){};
       const unsigned char* krow = kt + r32 * Lay::kKPitch + half * DS * 16;
@@ -216,10 +233,11 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       lr_part += lrsum;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const unsigned char* vrow = vt + (db * 32 + r32) * Lay::kVPitch + half * 16;
+        const int vr = db * 32 + r32;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(vrow + ks * 32);
+          u32x4_t a =
+              *reinterpret_cast<const u32x4_t*>(vt + vt_off32<Lay::kVPitch>(vr, 16 * ks + 8 * half));
           oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
         }
       }

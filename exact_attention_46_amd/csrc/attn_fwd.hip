@@ -28,6 +28,11 @@
 // sum of the 16-bit P values that actually enter the P V product (to normalise
 // O). With the latter the weights applied to V sum to exactly one, so the
 // rounding of a dominant P cancels instead of scaling its V row.
+//
+// Global reads go through raw buffer resources sized to the valid rows, so the
+// rows of a ragged last tile (and the Q rows past Nq) read as zero with no
+// per-row branch; K/V tiles are prefetched into registers one tile ahead and
+// written to LDS after the current tile's products.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -41,21 +46,23 @@ constexpr float kTau = 8.0f;    // lazy-rescale threshold, log2 units
 template <int D>
 struct FwdLayout {
   static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
-  static constexpr int kKeysPerThread = D / 32;         // rows each thread stages
   static constexpr int kKPitch = D * 2 + 16;            // K tile row pitch, bytes
   static constexpr int kKBytes = kFwdBN * kKPitch;
   static constexpr int kVPitch = kFwdBN * 2 + 16;       // V^T tile row pitch, bytes
   static constexpr int kVBytes = D * kVPitch;
   static constexpr int kStage = kKBytes + kVBytes;
   static constexpr int kLds = 2 * kStage;
+  // Staging roles: threads [0, 128) stage K, threads [128, 128 + D) stage V.
+  static constexpr int kKRowsPerThread = kFwdBN * kChunks / 128;  // D/16
+  static constexpr int kVThreads = 8 * (D / 8);                   // 8 slots x D/8 blocks
 };
 
-// Position of key offset o (0..15) inside its 16-key group of the V^T tile:
-// bits 2 and 3 swapped, so the eight keys an MFMA lane-half needs for one
-// 16-key step are contiguous (see the P^T operand layout below).
-__device__ __forceinline__ int vt_pos(int key) {
-  int o = key & 15;
-  return (key & ~15) | ((o & 4) << 1) | ((o & 8) >> 1) | (o & 3);
+// V^T tile: row d holds the 64 keys of the tile in 8 slots of 16 bytes. Slot s
+// = 2*grp + hh holds the keys 16*grp + {4*hh + 0..3, 8 + 4*hh + 0..3}: exactly
+// the 8 k-slots that MFMA lane-half hh consumes in the 16-key step grp (see the
+// P^T operand layout), so every MFMA A-operand is one 16-byte read.
+__device__ __forceinline__ int vslot_key(int s, int m) {
+  return 16 * (s >> 1) + 8 * (m >> 2) + 4 * (s & 1) + (m & 3);
 }
 
 // Maps the linear workgroup id to (batch*head unit, query tile). Heaviest causal
@@ -83,14 +90,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                 float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
   using Lay = FwdLayout<D>;
-  constexpr int KPT = Lay::kKeysPerThread;
   constexpr int DS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
+  constexpr int ROW = D * 2;   // bytes per row
   __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  // The wave index through readfirstlane: a scalar, so everything derived
+  // from it (rows of the wave, staging role) is known to be wave-uniform.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int half = lane >> 5;
 
@@ -102,83 +111,84 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int h = unit % Hq;
   const int g = h / group;  // == floor(h * Hkv / Hq) since Hq % Hkv == 0
 
-  const int64_t off = (int64_t)Nk - Nq;  // bottom-right causal alignment
+  const int off = Nk - Nq;  // bottom-right causal alignment
   const int q0 = qtile * kFwdBM;
-  const int qw0 = q0 + wave * 32;        // first query row of this wave
+  const int qw0 = q0 + wave * 32;  // first query row of this wave
   const int my_row = qw0 + r32;
 
   const uint16_t* qh = q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
   const uint16_t* kh = k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
   const uint16_t* vh = v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  const auto rq = make_rsrc(qh, (uint32_t)Nq * ROW);
+  const auto rk = make_rsrc(kh, (uint32_t)Nk * ROW);
+  const auto rv = make_rsrc(vh, (uint32_t)Nk * ROW);
 
   // Keys this workgroup can see: [0, kv_end).
-  int64_t kv_end = Nk;
+  int kv_end = Nk;
   if (CAUSAL) {
-    int64_t last_row = (int64_t)min(q0 + kFwdBM, Nq) - 1;
-    kv_end = last_row + off + 1;
-    if (kv_end < 0) kv_end = 0;
-    if (kv_end > Nk) kv_end = Nk;
+    kv_end = min(q0 + kFwdBM, Nq) - 1 + off + 1;
+    kv_end = max(0, min(kv_end, Nk));
   }
-  const int n_tiles = (int)((kv_end + kFwdBN - 1) / kFwdBN);
+  const int n_tiles = (kv_end + kFwdBN - 1) / kFwdBN;
 
-  // ---- Q^T operand: lane holds row my_row, d-chunk (half * DS + ds) for step ds.
+  // ---- Q^T operand: lane holds row my_row, d-chunk (half * DS + ds) for step ds
+  // (rows past Nq read as zero).
   u32x4_t qf[DS];
-  {
-    const bool ok = my_row < Nq;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(qh + (int64_t)(ok ? my_row : 0) * D);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      u32x4_t x = src[half * DS + ds];
-      qf[ds] = ok ? x : (u32x4_t){0u, 0u, 0u, 0u};
-    }
-  }
+  for (int ds = 0; ds < DS; ++ds)
+    qf[ds] = buf_load16(rq, (uint32_t)my_row * ROW + (half * DS + ds) * 16);
 
-  // ---- K/V staging: thread covers chunk c of rows a*KPT .. a*KPT+KPT-1.
-  const int st_c = tid % Lay::kChunks;
-  const int st_a = tid / Lay::kChunks;
-  u32x4_t kreg[KPT], vreg[KPT];
+  // ---- K/V staging, in two wave-uniform roles (measured on gfx950: 16-byte
+  // LDS writes whose 8- or 16-lane groups cover contiguous 128/256-byte runs
+  // are conflict-free at any row stride).
+  //  K role (threads 0..127): chunk kc of the consecutive rows ka*KR .. +KR-1,
+  //    one whole 256-byte row per 16 lanes and write instruction.
+  //  V role (threads 128..): V^T slot vs of d-block vd (d = 8*vd .. +7): loads
+  //    the slot's 8 key rows (16 bytes each), transposes the 8x8 block in
+  //    registers and writes 8 whole slots (rows d = 8*vd + e).
+  constexpr int KR = Lay::kKRowsPerThread;
+  const bool k_role = wave < 2;
+  const bool v_role = !k_role && wave < 2 + Lay::kVThreads / 64;
+  const int kc = tid % Lay::kChunks;
+  const int ka = (tid & 127) / Lay::kChunks;
+  const int vs = (tid - 128) & 7;
+  const int vd = ((tid - 128) >> 3) & (D / 8 - 1);
+  uint32_t st_off[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    st_off[i] = k_role ? (uint32_t)(ka * KR + (i % KR)) * ROW + kc * 16
+                       : (uint32_t)vslot_key(vs, i) * ROW + vd * 16;
+  u32x4_t sreg[8];
 
   auto gload = [&](int t) {
+    const uint32_t base = (uint32_t)t * (kFwdBN * ROW);
+    if (k_role) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int64_t key = (int64_t)t * kFwdBN + st_a * KPT + i;
-      if (key < Nk) {
-        kreg[i] = *reinterpret_cast<const u32x4_t*>(kh + key * D + st_c * 8);
-        vreg[i] = *reinterpret_cast<const u32x4_t*>(vh + key * D + st_c * 8);
-      } else {
-        kreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-        vreg[i] = (u32x4_t){0u, 0u, 0u, 0u};
-      }
+      for (int i = 0; i < KR; ++i) sreg[i] = buf_load16(rk, base + st_off[i]);
+    } else if (v_role) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(rv, base + st_off[i]);
     }
   };
 
   auto lds_store = [&](int buf) {
     unsigned char* kt = smem + buf * Lay::kStage;
     unsigned char* vt = kt + Lay::kKBytes;
+    if (k_role) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      *reinterpret_cast<u32x4_t*>(kt + (st_a * KPT + i) * Lay::kKPitch + st_c * 16) = kreg[i];
-    }
-    // V^T: for each of the 8 d values of the chunk, the KPT keys side by side.
-    const int pos = vt_pos(st_a * KPT);
+      for (int i = 0; i < KR; ++i)
+        *reinterpret_cast<u32x4_t*>(kt + (ka * KR + i) * Lay::kKPitch + kc * 16) = sreg[i];
+    } else if (v_role) {
+      // Row e of the block: element e of each of the 8 keys, two keys per dword.
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int dd = st_c * 8 + e;
-      unsigned char* dst = vt + dd * Lay::kVPitch + pos * 2;
-      if constexpr (KPT == 4) {
-        uint32_t w0, w1;
-        if (e & 1) {
-          w0 = hi_halves(vreg[0][e >> 1], vreg[1][e >> 1]);
-          w1 = hi_halves(vreg[2][e >> 1], vreg[3][e >> 1]);
-        } else {
-          w0 = lo_halves(vreg[0][e >> 1], vreg[1][e >> 1]);
-          w1 = lo_halves(vreg[2][e >> 1], vreg[3][e >> 1]);
-        }
-        *reinterpret_cast<u32x2_t*>(dst) = (u32x2_t){w0, w1};
-      } else {
-        uint32_t w0 = (e & 1) ? hi_halves(vreg[0][e >> 1], vreg[1][e >> 1])
-                              : lo_halves(vreg[0][e >> 1], vreg[1][e >> 1]);
-        *reinterpret_cast<uint32_t*>(dst) = w0;
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        u32x4_t out;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          out[j] = (e & 1) ? hi_halves(sreg[2 * j][w], sreg[2 * j + 1][w])
+                           : lo_halves(sreg[2 * j][w], sreg[2 * j + 1][w]);
+        *reinterpret_cast<u32x4_t*>(vt + (vd * 8 + e) * Lay::kVPitch + vs * 16) = out;
       }
     }
   };
@@ -192,23 +202,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 #pragma unroll
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
 
-  const int64_t row_kmax = CAUSAL ? (int64_t)my_row + off : (int64_t)Nk - 1;
+  // Largest key index this row may see (may be negative: then nothing).
+  const int row_kmax = CAUSAL ? min(my_row + off, Nk - 1) : Nk - 1;
   const bool wave_rows_valid = qw0 < Nq;
-  const int64_t wave_last_row = (int64_t)min(qw0 + 31, Nq - 1);
+  const int wave_last_row = min(qw0 + 31, Nq - 1);
 
-  if (n_tiles > 0) {
-    gload(0);
-    lds_store(0);
-  }
+  // The prologue and every iteration load and store unconditionally (the
+  // prefetch index is clamped to the last tile, an L2 hit), so every buffer
+  // load is provably complete at the loop head and the products of a tile never
+  // wait on the next tile's prefetch. All loads are in bounds or read as zero.
+  gload(0);
+  lds_store(0);
+  wait_all_memory();
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < n_tiles) gload(t + 1);
+    gload(min(t + 1, n_tiles - 1));
 
-    const int64_t k0 = (int64_t)t * kFwdBN;
-    const bool active =
-        wave_rows_valid && (!CAUSAL || k0 <= wave_last_row + off);
+    const int k0 = t * kFwdBN;
+    const bool active = wave_rows_valid && (!CAUSAL || k0 <= wave_last_row + off);
     if (active) {
       const unsigned char* kt = smem + buf * Lay::kStage;
       const unsigned char* vt = kt + Lay::kKBytes;
@@ -227,17 +240,15 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
 
       // Mask keys past the end and (causal) keys after the row's limit.
-      const bool need_mask =
-          (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > (int64_t)qw0 + off);
+      // Element e of block kb holds key k0 + 32*kb + 4*half + 8*(e/4) + e%4.
+      const bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          const int lim = row_kmax - (k0 + kb * 32 + 4 * half);
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int64_t key = k0 + kb * 32 + 8 * (e >> 2) + 4 * half + (e & 3);
-            const bool dead = (key >= Nk) || (key > row_kmax);
-            s[kb][e] = dead ? -INFINITY : s[kb][e];
-          }
+          for (int e = 0; e < 16; ++e)
+            s[kb][e] = (8 * (e >> 2) + (e & 3) > lim) ? -INFINITY : s[kb][e];
         }
       }
 
@@ -293,22 +304,24 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
       // O^T += V^T * P^T: 16-key steps; lane-half `half` reads the 8 keys
       // 16*ks + {8*(m/4) + 4*half + m%4}, stored contiguously at 16*ks + 8*half.
+      // V^T rows d = db*32 + r32, slot 2*ks + half.
+      const unsigned char* vbase = vt + r32 * Lay::kVPitch + half * 16;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const unsigned char* vrow = vt + (db * 32 + r32) * Lay::kVPitch + half * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(vrow + ks * 32);
+          u32x4_t a = *reinterpret_cast<const u32x4_t*>(vbase + db * 32 * Lay::kVPitch + ks * 32);
           oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
         }
       }
     }
 
-    if (t + 1 < n_tiles) lds_store(buf ^ 1);
+    lds_store(buf ^ 1);
+    wait_all_memory();
     __syncthreads();
   }
 
-  // ---- epilogue: O = O^T / l, LSE = ln2 * (m + log2 l).
+  // ---- epilogue: O = O^T / l_rounded, LSE = ln2 * (m + log2 l).
   const float l_row = sum_with_partner32(l_part);
   const float lr_row = sum_with_partner32(lr_part);
   if (my_row < Nq) {

@@ -52,12 +52,21 @@ __device__ __forceinline__ uint32_t pack2(float x, float y) {
   }
 }
 
-// The value of the partner lane (l ^ 32) combined with this lane's value.
+// This lane's value combined with that of its partner lane l ^ 32, through
+// v_permlane32_swap (a VALU lane swap between the two 32-lane halves, no LDS
+// round trip). Passing x as both operands, result[0] holds, in lanes 32..63,
+// the low half's values and result[1] holds, in lanes 0..31, the high half's
+// values; in the other lanes each holds x itself, so combining the two gives
+// f(x_l, x_{l^32}) in every lane.
 __device__ __forceinline__ float max_with_partner32(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_with_partner32(float x) {
-  return x + __shfl_xor(x, 32, 64);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Lane-halves of two dwords: {lo16(a), lo16(b)} and {hi16(a), hi16(b)}.
@@ -79,6 +88,27 @@ __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
                                   __builtin_bit_cast(f16x2_t, 0x3c003c00u), acc, false);
   }
 }
+
+// Buffer resource for a raw (stride 0) buffer of `bytes` bytes at `base`. Loads
+// through it at byte offsets >= bytes return zero instead of touching memory,
+// which is how ragged tiles are zero-filled without per-row branches.
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format word
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferWord3);
+}
+
+// 16-byte load at byte offset `off` (zero when off lies past the buffer end).
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Waits for every outstanding memory operation of this wave (vector memory,
+// LDS, scalar memory). Placed where those operations must be complete anyway
+// (before a barrier that publishes LDS stores fed by global loads), it also
+// tells the compiler's wait-count tracking that nothing is pending afterwards.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -39,7 +39,8 @@ extern "C" {
 /* Status codes. */
 #define MI355ATTN_OK 0
 #define MI355ATTN_ERR_NULL_PTR (-1)    /* a required pointer is NULL */
-#define MI355ATTN_ERR_BAD_SHAPE (-2)   /* a size <= 0, Hq % Hkv != 0, or a grid too large */
+#define MI355ATTN_ERR_BAD_SHAPE (-2)   /* a size <= 0, Hq % Hkv != 0, a sequence longer than
+                                          2^23 (Nq, Nk, max_len), or a grid too large */
 #define MI355ATTN_ERR_UNSUPPORTED (-3) /* d not in {64, 128}, unknown dtype, Hq/Hkv > 32 in decode */
 #define MI355ATTN_ERR_MISALIGNED (-4)  /* a pointer breaks the alignment rule above */
 #define MI355ATTN_ERR_BAD_ARG (-5)     /* scale not finite or <= 0, causal not 0/1 */

@@ -74,6 +74,7 @@ def fwd(lib, q=A, k=A, v=A, o=A2, lse=A2, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, d=128, s
     (dict(lse=None), -1),
     (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=0), -2), (dict(Nq=0), -2), (dict(Nk=-1), -2),
     (dict(Hq=3, Hkv=2), -2), (dict(B=2**30, Hq=2**10, Nq=128 * 4), -2),
+    (dict(Nq=2**23 + 1), -2), (dict(Nk=2**23 + 1), -2),
     (dict(d=96), -3), (dict(d=256), -3), (dict(dtype=2), -3),
     (dict(scale=0.0), -5), (dict(scale=-1.0), -5), (dict(scale=float("nan")), -5),
     (dict(scale=float("inf")), -5), (dict(causal=2), -5),
@@ -94,7 +95,7 @@ def split(lib, q=A, kc=A, vc=A, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2, max_len=6
     (dict(B=0), -2), (dict(max_len=0), -2), (dict(chunk=0), -2), (dict(Hq=6, Hkv=4), -2),
     (dict(d=80), -3), (dict(dtype=5), -3), (dict(Hq=66, Hkv=2), -3),
     (dict(scale=0.0), -5), (dict(kc=MIS), -4), (dict(sl=ctypes.c_void_p(4098)), -4),
-    (dict(B=2**20, Hkv=2**10, max_len=2**20, chunk=1), -2),
+    (dict(B=2**20, Hkv=2**10, max_len=2**20, chunk=1), -2), (dict(max_len=2**23 + 1), -2),
 ])
 def test_attn_decode_split_rejects(lib, kw, code):
     assert split(lib, **kw) == code
