@@ -29,10 +29,14 @@
 // O). With the latter the weights applied to V sum to exactly one, so the
 // rounding of a dominant P cancels instead of scaling its V row.
 //
-// Global reads go through raw buffer resources sized to the valid rows, so the
-// rows of a ragged last tile (and the Q rows past Nq) read as zero with no
-// per-row branch; K/V tiles are prefetched into registers one tile ahead and
-// written to LDS after the current tile's products.
+// Memory path. K and V tiles go from HBM straight into LDS with buffer loads
+// (no VGPR staging): each wave moves 1 KB per instruction, the buffer resource
+// of a tile covers only its valid rows, so the rows of a ragged last tile land
+// as zeros. Both tiles are stored row-major without padding; the 16-byte chunk
+// index inside a row is XOR-swizzled by a function of the row so that the MFMA
+// operand reads are conflict-free (measured on gfx950). K operands are 16-byte
+// reads; V^T operands come from two ds_read_b64_tr_b16 per MFMA, whose
+// 16-lane transpose turns row-major V into the key-major A-operand layout.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -45,24 +49,28 @@ constexpr float kTau = 8.0f;    // lazy-rescale threshold, log2 units
 
 template <int D>
 struct FwdLayout {
-  static constexpr int kChunks = D / 8;                 // 16-byte chunks per row
-  static constexpr int kKPitch = D * 2 + 16;            // K tile row pitch, bytes
-  static constexpr int kKBytes = kFwdBN * kKPitch;
-  static constexpr int kVPitch = kFwdBN * 2 + 16;       // V^T tile row pitch, bytes
-  static constexpr int kVBytes = D * kVPitch;
-  static constexpr int kStage = kKBytes + kVBytes;
+  static constexpr int kRow = D * 2;                 // bytes per row
+  static constexpr int kChunks = D / 8;              // 16-byte chunks per row
+  static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one wave load covers
+  static constexpr int kLoadsPerWave = kFwdBN / kRowsPerLoad / 4;  // per tensor
+  static constexpr int kTile = kFwdBN * kRow;        // bytes of one K or V tile
+  static constexpr int kStage = 2 * kTile;           // K tile then V tile
   static constexpr int kLds = 2 * kStage;
-  // Staging roles: threads [0, 128) stage K, threads [128, 128 + D) stage V.
-  static constexpr int kKRowsPerThread = kFwdBN * kChunks / 128;  // D/16
-  static constexpr int kVThreads = 8 * (D / 8);                   // 8 slots x D/8 blocks
 };
 
-// V^T tile: row d holds the 64 keys of the tile in 8 slots of 16 bytes. Slot s
-// = 2*grp + hh holds the keys 16*grp + {4*hh + 0..3, 8 + 4*hh + 0..3}: exactly
-// the 8 k-slots that MFMA lane-half hh consumes in the 16-key step grp (see the
-// P^T operand layout), so every MFMA A-operand is one 16-byte read.
-__device__ __forceinline__ int vslot_key(int s, int m) {
-  return 16 * (s >> 1) + 8 * (m >> 2) + 4 * (s & 1) + (m & 3);
+// Chunk swizzles (chunk index XOR f(row)), chosen against the LDS bank layout
+// (64 four-byte banks; a 256-byte window is one bank row):
+//  K: 32 lanes read 16 bytes of rows r..r+31 at one logical chunk; 16
+//     consecutive rows must hit 16 distinct 16-byte bank groups.
+//  V: each 32-lane half of a transposing read covers 4 consecutive rows x 64
+//     bytes; the 4 rows must land on 4 disjoint 64-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
 // Maps the linear workgroup id to (batch*head unit, query tile). Heaviest causal
@@ -92,13 +100,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   using Lay = FwdLayout<D>;
   constexpr int DS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  constexpr int ROW = D * 2;   // bytes per row
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Lay::kLds];
+  constexpr int ROW = Lay::kRow;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[Lay::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // The wave index through readfirstlane: a scalar, so everything derived
-  // from it (rows of the wave, staging role) is known to be wave-uniform.
+  // from it is known to be wave-uniform.
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31;
   const int half = lane >> 5;
@@ -120,8 +128,6 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const uint16_t* kh = k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
   const uint16_t* vh = v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
   const auto rq = make_rsrc(qh, (uint32_t)Nq * ROW);
-  const auto rk = make_rsrc(kh, (uint32_t)Nk * ROW);
-  const auto rv = make_rsrc(vh, (uint32_t)Nk * ROW);
 
   // Keys this workgroup can see: [0, kv_end).
   int kv_end = Nk;
@@ -138,60 +144,50 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int ds = 0; ds < DS; ++ds)
     qf[ds] = buf_load16(rq, (uint32_t)my_row * ROW + (half * DS + ds) * 16);
 
-  // ---- K/V staging, in two wave-uniform roles (measured on gfx950: 16-byte
-  // LDS writes whose 8- or 16-lane groups cover contiguous 128/256-byte runs
-  // are conflict-free at any row stride).
-  //  K role (threads 0..127): chunk kc of the consecutive rows ka*KR .. +KR-1,
-  //    one whole 256-byte row per 16 lanes and write instruction.
-  //  V role (threads 128..): V^T slot vs of d-block vd (d = 8*vd .. +7): loads
-  //    the slot's 8 key rows (16 bytes each), transposes the 8x8 block in
-  //    registers and writes 8 whole slots (rows d = 8*vd + e).
-  constexpr int KR = Lay::kKRowsPerThread;
-  const bool k_role = wave < 2;
-  const bool v_role = !k_role && wave < 2 + Lay::kVThreads / 64;
-  const int kc = tid % Lay::kChunks;
-  const int ka = (tid & 127) / Lay::kChunks;
-  const int vs = (tid - 128) & 7;
-  const int vd = ((tid - 128) >> 3) & (D / 8 - 1);
-  uint32_t st_off[8];
+  // ---- tile loads: load i of wave w covers tile rows (w*LPW + i)*RPL ..
+  // +RPL-1; lane p fills physical chunk p % C of row p / C, i.e. it loads
+  // logical chunk (p % C) ^ swz(row). Offsets are relative to the tile's first
+  // row, whose address is carried by the per-tile buffer resource.
+  constexpr int LPW = Lay::kLoadsPerWave;
+  constexpr int RPL = Lay::kRowsPerLoad;
+  uint32_t koff[LPW], voff[LPW];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    st_off[i] = k_role ? (uint32_t)(ka * KR + (i % KR)) * ROW + kc * 16
-                       : (uint32_t)vslot_key(vs, i) * ROW + vd * 16;
-  u32x4_t sreg[8];
-
-  auto gload = [&](int t) {
-    const uint32_t base = (uint32_t)t * (kFwdBN * ROW);
-    if (k_role) {
+  for (int i = 0; i < LPW; ++i) {
+    const int row = (wave * LPW + i) * RPL + lane / Lay::kChunks;
+    const int pc = lane % Lay::kChunks;
+    koff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
+    voff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ v_swz<D>(row)) * 16);
+  }
+  auto issue_tile = [&](int t, int stage) {
+    const int r0 = t * kFwdBN;  // < Nk for every tile that is issued
+    const uint32_t valid = (uint32_t)(Nk - r0) * ROW;
+    const auto rk = make_rsrc(kh + (int64_t)r0 * D, valid);
+    const auto rv = make_rsrc(vh + (int64_t)r0 * D, valid);
+    unsigned char* kt = smem + stage * Lay::kStage;
+    unsigned char* vt = kt + Lay::kTile;
 #pragma unroll
-      for (int i = 0; i < KR; ++i) sreg[i] = buf_load16(rk, base + st_off[i]);
-    } else if (v_role) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(rv, base + st_off[i]);
+    for (int i = 0; i < LPW; ++i) {
+      buf_load16_lds(rk, kt + (wave * LPW + i) * 1024, koff[i]);
+      buf_load16_lds(rv, vt + (wave * LPW + i) * 1024, voff[i]);
     }
   };
 
-  auto lds_store = [&](int buf) {
-    unsigned char* kt = smem + buf * Lay::kStage;
-    unsigned char* vt = kt + Lay::kKBytes;
-    if (k_role) {
+  // ---- per-lane LDS operand offsets (relative to the tile base)
+  // K: row 32*kb + r32, logical chunk half*DS + ds, physical chunk ^ k_swz(r32).
+  const int kx = k_swz<D>(r32);
+  // V (transposing read): in each 16-lane group, source lane j = 4*kk + a
+  // addresses row 16*ks + 4*half + kk (+8 for the second read) at column
+  // d = 32*db + 16*((lane >> 4) & 1) + 4*a. The swizzle of those rows equals
+  // v_swz(4*half + kk) for every ks and for the +8 rows.
+  const int vkk = (lane & 15) >> 2, va = lane & 3;
+  const int vrow0 = 4 * half + vkk;
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * va;
+  uint32_t vop[DB];
 #pragma unroll
-      for (int i = 0; i < KR; ++i)
-        *reinterpret_cast<u32x4_t*>(kt + (ka * KR + i) * Lay::kKPitch + kc * 16) = sreg[i];
-    } else if (v_role) {
-      // Row e of the block: element e of each of the 8 keys, two keys per dword.
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        u32x4_t out;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          out[j] = (e & 1) ? hi_halves(sreg[2 * j][w], sreg[2 * j + 1][w])
-                           : lo_halves(sreg[2 * j][w], sreg[2 * j + 1][w]);
-        *reinterpret_cast<u32x4_t*>(vt + (vd * 8 + e) * Lay::kVPitch + vs * 16) = out;
-      }
-    }
-  };
+  for (int db = 0; db < DB; ++db) {
+    const int col = 32 * db + vcol;
+    vop[db] = (uint32_t)(vrow0 * ROW + (((col >> 3) ^ v_swz<D>(vrow0)) * 16) + (col & 7) * 2);
+  }
 
   // ---- per-row state (identical in lanes l and l ^ 32)
   const float c = scale * kLog2e;
@@ -207,34 +203,30 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const bool wave_rows_valid = qw0 < Nq;
   const int wave_last_row = min(qw0 + 31, Nq - 1);
 
-  // The prologue and every iteration load and store unconditionally (the
-  // prefetch index is clamped to the last tile, an L2 hit), so every buffer
-  // load is provably complete at the loop head and the products of a tile never
-  // wait on the next tile's prefetch. All loads are in bounds or read as zero.
-  gload(0);
-  lds_store(0);
+  if (n_tiles > 0) issue_tile(0, 0);
   wait_all_memory();
   __syncthreads();
 
   for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    gload(min(t + 1, n_tiles - 1));
+    const int stage = t & 1;
+    // The other stage was last read in iteration t-1, before its barrier.
+    if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
 
     const int k0 = t * kFwdBN;
     const bool active = wave_rows_valid && (!CAUSAL || k0 <= wave_last_row + off);
     if (active) {
-      const unsigned char* kt = smem + buf * Lay::kStage;
-      const unsigned char* vt = kt + Lay::kKBytes;
+      const unsigned char* kt = smem + stage * Lay::kStage;
+      const unsigned char* vt = kt + Lay::kTile;
 
       // S^T = K * Q^T for two 32-key blocks.
       f32x16_t s[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb] = (f32x16_t){};
-        const unsigned char* krow = kt + (kb * 32 + r32) * Lay::kKPitch + half * DS * 16;
+        const unsigned char* krow = kt + (kb * 32 + r32) * ROW;
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + ds * 16);
+          u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (((half * DS + ds) ^ kx) << 4));
           s[kb] = mfma32x32x16<DT>(a, qf[ds], s[kb]);
         }
       }
@@ -302,22 +294,24 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
       lr_part += lrsum;
 
-      // O^T += V^T * P^T: 16-key steps; lane-half `half` reads the 8 keys
-      // 16*ks + {8*(m/4) + 4*half + m%4}, stored contiguously at 16*ks + 8*half.
-      // V^T rows d = db*32 + r32, slot 2*ks + half.
-      const unsigned char* vbase = vt + r32 * Lay::kVPitch + half * 16;
+      // O^T += V^T * P^T. For step ks the lane-half `half` needs, in k-slot m,
+      // key 16*ks + 8*(m/4) + 4*half + m%4: the first transposing read gives
+      // slots 0..3 (rows 16*ks + 4*half + 0..3), the second slots 4..7 (8 rows
+      // further).
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
+      for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(vbase + db * 32 * Lay::kVPitch + ks * 32);
+        for (int db = 0; db < DB; ++db) {
+          const unsigned char* p0 = vt + vop[db] + ks * 16 * ROW;
+          const u32x2_t lo = lds_read_tr16(p0);
+          const u32x2_t hi = lds_read_tr16(p0 + 8 * ROW);
+          const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
           oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
         }
       }
     }
 
-    lds_store(buf ^ 1);
-    wait_all_memory();
+    wait_all_memory();  // the next tile has landed in LDS
     __syncthreads();
   }
 

@@ -104,6 +104,27 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16-byte load from a raw buffer straight into LDS: lane p's 16 bytes land at
+// lds_base + 16 * p (lds_base must be the same for the whole wave); offsets
+// past the buffer end write zeros. Completion is counted by vmcnt.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
+                                               uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+
+// Transposing LDS read of four 16-bit values (gfx950 ds_read_b64_tr_b16).
+// Within each 16-lane group, source lane j = 4k + a supplies the address of 4
+// consecutive elements; output lane i = 4a + c receives element c of source
+// lanes 4k + a for k = 0..3 (element k of the result).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
 // Waits for every outstanding memory operation of this wave (vector memory,
 // LDS, scalar memory). Placed where those operations must be complete anyway
 // (before a barrier that publishes LDS stores fed by global loads), it also
