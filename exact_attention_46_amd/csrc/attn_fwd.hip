@@ -6,8 +6,8 @@
 //
 // Work decomposition
 //   one workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
-//   32 query rows for the whole pass. K/V tiles of 64 keys stream through
-//   double-buffered LDS and are shared by the 4 waves.
+//   32 query rows for the whole pass. K/V tiles of 64 keys stream through LDS
+//   (two K and two V buffers) and are shared by the 4 waves.
 //
 // Per wave and K/V tile (both products on 32x32x16 MFMA, fp32 accumulate):
 //   S^T[64 keys x 32 rows] = K_tile * Q_w^T      A = K from LDS, B = Q^T in VGPRs
@@ -37,6 +37,12 @@
 // operand reads are conflict-free (measured on gfx950). K operands are 16-byte
 // reads; V^T operands come from two ds_read_b64_tr_b16 per MFMA, whose
 // 16-lane transpose turns row-major V into the key-major A-operand layout.
+//
+// Software pipeline. Iteration t issues S(t+1) = K(t+1) Q^T before the softmax
+// of S(t) and O += V(t) P(t), so the next tile's products do not wait for this
+// tile's softmax. K runs two tiles ahead of V: iteration t loads K(t+2) into
+// the buffer K(t) occupied and V(t+1) into the buffer of V(t-1); one barrier
+// per iteration publishes both.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,8 +60,7 @@ struct FwdLayout {
   static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one wave load covers
   static constexpr int kLoadsPerWave = kFwdBN / kRowsPerLoad / 4;  // per tensor
   static constexpr int kTile = kFwdBN * kRow;        // bytes of one K or V tile
-  static constexpr int kStage = 2 * kTile;           // K tile then V tile
-  static constexpr int kLds = 2 * kStage;
+  static constexpr int kLds = 4 * kTile;             // two K and two V buffers
 };
 
 // Chunk swizzles (chunk index XOR f(row)), chosen against the LDS bank layout
@@ -158,18 +163,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     koff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
     voff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ v_swz<D>(row)) * 16);
   }
-  auto issue_tile = [&](int t, int stage) {
+  // LDS: K buffers at [0, 2*kTile), V buffers at [2*kTile, 4*kTile).
+  unsigned char* kbuf = smem;
+  unsigned char* vbuf = smem + 2 * Lay::kTile;
+  auto issue_k = [&](int t) {
     const int r0 = t * kFwdBN;  // < Nk for every tile that is issued
-    const uint32_t valid = (uint32_t)(Nk - r0) * ROW;
-    const auto rk = make_rsrc(kh + (int64_t)r0 * D, valid);
-    const auto rv = make_rsrc(vh + (int64_t)r0 * D, valid);
-    unsigned char* kt = smem + stage * Lay::kStage;
-    unsigned char* vt = kt + Lay::kTile;
+    const auto rk = make_rsrc(kh + (int64_t)r0 * D, (uint32_t)(Nk - r0) * ROW);
+    unsigned char* dst = kbuf + (t & 1) * Lay::kTile;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      buf_load16_lds(rk, kt + (wave * LPW + i) * 1024, koff[i]);
-      buf_load16_lds(rv, vt + (wave * LPW + i) * 1024, voff[i]);
-    }
+    for (int i = 0; i < LPW; ++i) buf_load16_lds(rk, dst + (wave * LPW + i) * 1024, koff[i]);
+  };
+  auto issue_v = [&](int t) {
+    const int r0 = t * kFwdBN;
+    const auto rv = make_rsrc(vh + (int64_t)r0 * D, (uint32_t)(Nk - r0) * ROW);
+    unsigned char* dst = vbuf + (t & 1) * Lay::kTile;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) buf_load16_lds(rv, dst + (wave * LPW + i) * 1024, voff[i]);
   };
 
   // ---- per-lane LDS operand offsets (relative to the tile base)
@@ -203,117 +212,137 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const bool wave_rows_valid = qw0 < Nq;
   const int wave_last_row = min(qw0 + 31, Nq - 1);
 
-  if (n_tiles > 0) issue_tile(0, 0);
-  wait_all_memory();
-  __syncthreads();
+  // Tile t is active for this wave when some row of the wave may see key 64t.
+  auto active = [&](int t) {
+    return wave_rows_valid && (!CAUSAL || t * kFwdBN <= wave_last_row + off);
+  };
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int stage = t & 1;
-    // The other stage was last read in iteration t-1, before its barrier.
-    if (t + 1 < n_tiles) issue_tile(t + 1, stage ^ 1);
+  // S^T(t) = K(t) * Q^T for two 32-key blocks.
+  auto qk = [&](int t, f32x16_t* s) {
+    const unsigned char* kt = kbuf + (t & 1) * Lay::kTile;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16_t){};
+      const unsigned char* krow = kt + (kb * 32 + r32) * ROW;
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (((half * DS + ds) ^ kx) << 4));
+        s[kb] = mfma32x32x16<DT>(a, qf[ds], s[kb]);
+      }
+    }
+  };
 
+  // Softmax of S^T(t) into the P^T operands, then O^T += V(t)^T * P^T.
+  auto softmax_pv = [&](int t, f32x16_t* s) {
     const int k0 = t * kFwdBN;
-    const bool active = wave_rows_valid && (!CAUSAL || k0 <= wave_last_row + off);
-    if (active) {
-      const unsigned char* kt = smem + stage * Lay::kStage;
-      const unsigned char* vt = kt + Lay::kTile;
-
-      // S^T = K * Q^T for two 32-key blocks.
-      f32x16_t s[2];
+    const unsigned char* vt = vbuf + (t & 1) * Lay::kTile;
+    // Mask keys past the end and (causal) keys after the row's limit.
+    // Element e of block kb holds key k0 + 32*kb + 4*half + 8*(e/4) + e%4.
+    const bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
+    if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = (f32x16_t){};
-        const unsigned char* krow = kt + (kb * 32 + r32) * ROW;
+        const int lim = row_kmax - (k0 + kb * 32 + 4 * half);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) {
-          u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (((half * DS + ds) ^ kx) << 4));
-          s[kb] = mfma32x32x16<DT>(a, qf[ds], s[kb]);
-        }
-      }
-
-      // Mask keys past the end and (causal) keys after the row's limit.
-      // Element e of block kb holds key k0 + 32*kb + 4*half + 8*(e/4) + e%4.
-      const bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int lim = row_kmax - (k0 + kb * 32 + 4 * half);
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            s[kb][e] = (8 * (e >> 2) + (e & 3) > lim) ? -INFINITY : s[kb][e];
-        }
-      }
-
-      // Row maximum of this tile (raw scores; scale > 0 keeps the order).
-      float mx = s[0][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = max_with_partner32(mx);
-      const float m_tile = mx * c;
-
-      const bool grow = m_tile > m_used + kTau;
-      if (__any(grow)) {
-        const float m_new = grow ? m_tile : m_used;
-        const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
-        m_used = m_new;
-        l_part *= alpha;
-        lr_part *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
-      }
-      const float neg_m = (m_used == -INFINITY) ? 0.f : -m_used;
-
-      // P^T = exp2(s * c - m); the row sum uses the unrounded values.
-      u32x4_t pf[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float p[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          p[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, neg_m));
-          lsum += p[e];
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          pf[kb * 2 + j] = (u32x4_t){pack2<DT>(p[8 * j + 0], p[8 * j + 1]),
-                                     pack2<DT>(p[8 * j + 2], p[8 * j + 3]),
-                                     pack2<DT>(p[8 * j + 4], p[8 * j + 5]),
-                                     pack2<DT>(p[8 * j + 6], p[8 * j + 7])};
-        }
-      }
-      l_part += lsum;
-      float lrsum = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
-      lr_part += lrsum;
-
-      // O^T += V^T * P^T. For step ks the lane-half `half` needs, in k-slot m,
-      // key 16*ks + 8*(m/4) + 4*half + m%4: the first transposing read gives
-      // slots 0..3 (rows 16*ks + 4*half + 0..3), the second slots 4..7 (8 rows
-      // further).
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const unsigned char* p0 = vt + vop[db] + ks * 16 * ROW;
-          const u32x2_t lo = lds_read_tr16(p0);
-          const u32x2_t hi = lds_read_tr16(p0 + 8 * ROW);
-          const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
-        }
+        for (int e = 0; e < 16; ++e)
+          s[kb][e] = (8 * (e >> 2) + (e & 3) > lim) ? -INFINITY : s[kb][e];
       }
     }
 
-    wait_all_memory();  // the next tile has landed in LDS
-    __syncthreads();
+    // Row maximum of this tile (raw scores; scale > 0 keeps the order).
+    float mx = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    mx = max_with_partner32(mx);
+    const float m_tile = mx * c;
+
+    const bool grow = m_tile > m_used + kTau;
+    if (__any(grow)) {
+      const float m_new = grow ? m_tile : m_used;
+      const float alpha = grow ? fast_exp2(m_used - m_new) : 1.f;
+      m_used = m_new;
+      l_part *= alpha;
+      lr_part *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[db][e] *= alpha;
+    }
+    const float neg_m = (m_used == -INFINITY) ? 0.f : -m_used;
+
+    // P^T = exp2(s * c - m); the row sum uses the unrounded values.
+    u32x4_t pf[4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        p[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, neg_m));
+        lsum += p[e];
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        pf[kb * 2 + j] = (u32x4_t){pack2<DT>(p[8 * j + 0], p[8 * j + 1]),
+                                   pack2<DT>(p[8 * j + 2], p[8 * j + 3]),
+                                   pack2<DT>(p[8 * j + 4], p[8 * j + 5]),
+                                   pack2<DT>(p[8 * j + 6], p[8 * j + 7])};
+      }
+    }
+    l_part += lsum;
+    float lrsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
+    lr_part += lrsum;
+
+    // O^T += V^T * P^T. For step ks the lane-half `half` needs, in k-slot m,
+    // key 16*ks + 8*(m/4) + 4*half + m%4: the first transposing read gives
+    // slots 0..3 (rows 16*ks + 4*half + 0..3), the second slots 4..7 (8 rows
+    // further).
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const unsigned char* p0 = vt + vop[db] + ks * 16 * ROW;
+        const u32x2_t lo = lds_read_tr16(p0);
+        const u32x2_t hi = lds_read_tr16(p0 + 8 * ROW);
+        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
+      }
+    }
+  };
+
+  // Prologue: K(0), V(0), K(1) in flight; S(0) once they land.
+  f32x16_t sa[2], sb[2];
+  if (n_tiles > 0) {
+    issue_k(0);
+    issue_v(0);
   }
+  if (n_tiles > 1) issue_k(1);
+  wait_all_memory();
+  __syncthreads();
+  if (n_tiles > 0 && active(0)) qk(0, sa);
+
+  // One iteration: loads for t+2 (K) and t+1 (V), S(t+1), the softmax and P V
+  // of tile t, then the barrier that publishes the loads.
+  auto step = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
+    if (t + 2 < n_tiles) issue_k(t + 2);
+    if (t + 1 < n_tiles) issue_v(t + 1);
+    if (t + 1 < n_tiles && active(t + 1)) qk(t + 1, s_next);
+    if (active(t)) softmax_pv(t, s_cur);
+    wait_all_memory();
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t < n_tiles) step(t, sa, sb);
 
   // ---- epilogue: O = O^T / l_rounded, LSE = ln2 * (m + log2 l).
   const float l_row = sum_with_partner32(l_part);
