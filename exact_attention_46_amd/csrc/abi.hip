@@ -53,7 +53,9 @@ extern "C" int attn_decode_split(const void* q, const void* k_cache, const void*
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16) ||
       !aligned(part_lse, 4) || !aligned(seq_lens, 4))
     return MI355ATTN_ERR_MISALIGNED;
-  if (mi355attn::split_grid_blocks(B, Hkv, max_len, chunk) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  if (mi355attn::split_work_items(B, Hkv, max_len, chunk) > kMaxGrid ||
+      (int64_t)B * Hq * (((int64_t)max_len + chunk - 1) / chunk) > ((int64_t)1 << 40))
+    return MI355ATTN_ERR_BAD_SHAPE;
   mi355attn::SplitArgs a{q, k_cache, v_cache, seq_lens, part_o, part_lse, B, Hq, Hkv, max_len,
                          d, chunk, scale, dtype};
   return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));

@@ -129,7 +129,27 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 // LDS, scalar memory). Placed where those operations must be complete anyway
 // (before a barrier that publishes LDS stores fed by global loads), it also
 // tells the compiler's wait-count tracking that nothing is pending afterwards.
-__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+// The waits below are also scheduling barriers: LDS data written by buffer
+// loads to LDS is only visible after the wait, which the compiler cannot see.
+__device__ __forceinline__ void wait_all_memory() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).
+// Wait until at most N vector memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until every LDS operation of this wave has completed.
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

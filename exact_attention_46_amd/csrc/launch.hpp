@@ -42,7 +42,9 @@ struct CombineArgs {
 
 // Number of workgroups the forward launch uses (for the grid-size check).
 int64_t fwd_grid_blocks(int B, int Hq, int Nq);
-int64_t split_grid_blocks(int B, int Hkv, int max_len, int chunk);
+// Upper bound on the split kernel's work items (sequence, chunk, kv-head); the
+// kernel indexes them with 32-bit integers.
+int64_t split_work_items(int B, int Hkv, int max_len, int chunk);
 
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
