@@ -10,11 +10,20 @@
 //
 // Each wave owns whole items: it walks the items w, w + W, w + 2W, ... of the
 // list of valid items (chunk slots past the end of a sequence are not in the
-// list; the list is the prefix sum of ceil(L_b / chunk), computed by every wave
-// from seq_lens with ballots, so no workspace is needed). A wave streams its
-// items' K and V in 32-key tiles straight from HBM into its own two-stage LDS
-// ring (buffer loads to LDS, zero-filled past L_b), one tile ahead of the tile
-// it computes, across item boundaries too. No wave ever waits for another.
+// list; item i is kv-head i % Hkv of the (i / Hkv)-th valid chunk, counting
+// the chunks of all sequences in order). Since a wave visits its items in
+// increasing order, it finds their sequences with a cursor that only moves
+// forward, reading seq_lens with scalar loads; no workspace is needed.
+//
+// A wave streams its items' K and V in 32-key tiles straight from HBM into
+// its own two-stage LDS ring (buffer loads to LDS, non-temporal, zero-filled
+// past L_b), one tile ahead of the tile it computes, across item boundaries
+// too; the R query rows of the next item follow the same way into a Q slot of
+// the wave. No wave ever waits for another, and a wave waits only for the
+// tile it is about to use: vector-memory operations of a wave complete in
+// issue order, so "at most N outstanding" with N = the loads issued after the
+// tile (plus the partial-result stores issued after it at an item end) means
+// the tile has landed.
 //
 // Per tile: S^T[32 keys x 32 cols] = K Q^T (8 MFMAs 32x32x16), the running
 // max / sum update of the online softmax (the OnlineSoftmaxState of the
@@ -35,6 +44,7 @@ namespace mi355attn {
 constexpr int kSplitWaves = 4;        // waves per workgroup (one workgroup per CU)
 constexpr int kSplitThreads = 64 * kSplitWaves;
 constexpr int kSplitBN = 32;          // keys per tile
+constexpr int kSplitMaxGroup = 32;    // query heads per kv-head (the MFMA's columns)
 constexpr float kSplitTau = 8.0f;     // lazy-rescale threshold, log2 units
 
 template <int D>
@@ -45,9 +55,14 @@ struct SplitLayout {
   static constexpr int kLoads = kSplitBN / kRowsPerLoad;      // loads per tile and tensor
   static constexpr int kTile = kSplitBN * kRow;               // bytes of a K or V tile
   static constexpr int kStage = 2 * kTile;                    // K then V
-  static constexpr int kWave = 2 * kStage;                    // two stages per wave
+  static constexpr int kQ = kSplitMaxGroup * kRow;            // Q rows of one group
+  static constexpr int kWave = 2 * kStage + kQ;               // two stages + the Q slot
   static constexpr int kLds = kSplitWaves * kWave;
+  // Vector-memory stores at the end of an item, per wave: four 16-byte stores
+  // per 32 columns of O_c, and one for LSE_c.
+  static constexpr int kItemStores = 4 * (D / 32) + 1;
 };
+static_assert(SplitLayout<128>::kLds <= 160 * 1024, "LDS budget of a gfx950 workgroup");
 
 // Chunk swizzles as in the forward kernel (conflict-free MFMA operand reads).
 template <int D>
@@ -67,35 +82,6 @@ __device__ __forceinline__ int clamp_len(const int* seq_lens, int b, int max_len
 // Number of chunk slots of sequence b that hold keys.
 __device__ __forceinline__ int chunks_of(const int* seq_lens, int b, int max_len, int chunk) {
   return (int)(((int64_t)clamp_len(seq_lens, b, max_len) + chunk - 1) / chunk);
-}
-
-// Maps compact chunk index `idx` (the chunks of all sequences in order) to
-// (b, c), scanning the sequences 64 at a time with one lane per sequence.
-// Must be called by the whole wave; the result is the same in every lane.
-__device__ __forceinline__ void locate_chunk(const int* seq_lens, int B, int max_len, int chunk,
-                                             int idx, int lane, int& b_out, int& c_out) {
-  int base = 0;  // chunks of the sequences before this group of 64
-  b_out = B;
-  c_out = 0;
-  for (int b0 = 0; b0 < B; b0 += 64) {
-    const int b = b0 + lane;
-    const int n = b < B ? chunks_of(seq_lens, b, max_len, chunk) : 0;
-    int incl = n;  // inclusive prefix sum across the 64 lanes
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) {
-      const int y = __shfl_up(incl, sh, 64);
-      if (lane >= sh) incl += y;
-    }
-    const int total = __shfl(incl, 63, 64);
-    if (idx < base + total) {
-      // the sequence is the first lane whose inclusive prefix exceeds idx - base
-      const int lb = __popcll(__ballot(incl <= idx - base));
-      b_out = b0 + lb;
-      c_out = idx - base - __shfl(incl - n, lb, 64);
-      return;
-    }
-    base += total;
-  }
 }
 
 __device__ __forceinline__ int total_chunks(const int* seq_lens, int B, int max_len, int chunk,
@@ -122,6 +108,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int DB = D / 32;
   constexpr int ROW = Lay::kRow;
   constexpr int NL = Lay::kLoads;
+  constexpr int NS = Lay::kItemStores;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[Lay::kLds];
 
   const int tid = threadIdx.x;
@@ -141,8 +128,10 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if (cc >= chunks_of(seq_lens, bb, max_len, chunk)) part_lse[i] = -INFINITY;
   }
 
-  const int n_items = total_chunks(seq_lens, B, max_len, chunk, lane) * Hkv;
+  const int n_items =
+      __builtin_amdgcn_readfirstlane(total_chunks(seq_lens, B, max_len, chunk, lane) * Hkv);
   unsigned char* ring = smem + wave * Lay::kWave;
+  unsigned char* qslot = ring + 2 * Lay::kStage;
 
   // DMA offsets of this lane inside a tile (relative to the tile's first row):
   // load i covers rows i*RPL .. +RPL-1; lane p fills physical chunk p % C of
@@ -166,6 +155,16 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int col = 32 * db + vcol;
     vop[db] = (uint32_t)(vrow0 * ROW + (((col >> 3) ^ dv_swz<D>(vrow0)) * 16) + (col & 7) * 2);
   }
+  // Q^T operand: column r32 is query head g*R + r32. Columns r32 >= R repeat
+  // head g*R; their results are never written.
+  const uint32_t qop = (uint32_t)((r32 < R ? r32 : 0) * ROW + half * DS * 16);
+
+  // Sequence cursor of this wave (wave-uniform): sequence cb, whose first
+  // chunk is valid chunk number cbase, with cn chunks and length cl_len.
+  int cb = 0;
+  int cl_len = clamp_len(seq_lens, 0, max_len);
+  int cn = (cl_len + chunk - 1) / chunk;
+  int cbase = 0;
 
   // A work position: item, tile inside the item, and the item's geometry.
   struct Pos {
@@ -175,15 +174,23 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     p.item = item;
     p.tile = 0;
     if (item >= n_items) return false;
-    p.g = item % Hkv;
-    locate_chunk(seq_lens, B, max_len, chunk, item / Hkv, lane, p.b, p.c);
-    p.L = clamp_len(seq_lens, p.b, max_len);
+    const int idx = item / Hkv;
+    p.g = item - idx * Hkv;
+    while (idx >= cbase + cn) {  // terminates: idx < the total number of chunks
+      cbase += cn;
+      ++cb;
+      cl_len = clamp_len(seq_lens, cb, max_len);
+      cn = (cl_len + chunk - 1) / chunk;
+    }
+    p.b = cb;
+    p.c = idx - cbase;
+    p.L = cl_len;
     const int lo = p.c * chunk;
     const int hi = min(p.L, lo + chunk);
     p.n_tiles = (hi - lo + kSplitBN - 1) / kSplitBN;
     return true;
   };
-  auto issue = [&](const Pos& p, int stage) {
+  auto issue_kv = [&](const Pos& p, int stage) {
     const int r0 = p.c * chunk + p.tile * kSplitBN;  // < L for every issued tile
     const int64_t head = ((int64_t)p.b * Hkv + p.g) * (int64_t)max_len + r0;
     const uint32_t valid = (uint32_t)(p.L - r0) * ROW;  // rows past L read as zero
@@ -193,43 +200,39 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     unsigned char* vt = kt + Lay::kTile;
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
-      buf_load16_lds(rk, kt + i * 1024, koff[i]);
-      buf_load16_lds(rv, vt + i * 1024, voff[i]);
+      buf_load16_lds<kNonTemporal>(rk, kt + i * 1024, koff[i]);
+      buf_load16_lds<kNonTemporal>(rv, vt + i * 1024, voff[i]);
     }
+  };
+  // The R query rows of item p (contiguous in q) into the Q slot, row-major.
+  auto issue_q = [&](const Pos& p) {
+    const uint32_t bytes = (uint32_t)(R * ROW);
+    const auto rq = make_rsrc(q + ((int64_t)p.b * Hq + (int64_t)p.g * R) * D, bytes);
+    for (uint32_t off = 0; off < bytes; off += 1024)
+      buf_load16_lds(rq, qslot + off, off + (uint32_t)lane * 16);
   };
 
   const float cl = scale * kLog2e;
   u32x4_t qf[DS];
   float m_used = -INFINITY, l_part = 0.f, lr_part = 0.f;
   f32x16_t oacc[DB];
-  auto begin_item = [&](const Pos& p) {
-    // Q^T operand: column r32 is query head g*R + r32 (zero for r32 >= R).
-    const int rr = r32 < R ? r32 : 0;
-    const uint16_t* qrow = q + ((int64_t)p.b * Hq + (int64_t)p.g * R + rr) * D;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const u32x4_t x = reinterpret_cast<const u32x4_t*>(qrow)[half * DS + ds];
-      qf[ds] = r32 < R ? x : (u32x4_t){0u, 0u, 0u, 0u};
-    }
-    m_used = -INFINITY;
-    l_part = 0.f;
-    lr_part = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
-  };
+  for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
 
   Pos cur, nxt;
   bool have = locate(gwave, cur);
   if (have) {
-    issue(cur, 0);
-    begin_item(cur);
+    issue_kv(cur, 0);
+    issue_q(cur);
   }
   int stage = 0;
+  bool stores_out = false;  // the previous tile ended an item (its stores are in flight)
 
   while (have) {
     // The next position (next tile of this item, or the first tile of the
-    // wave's next item) goes out before this tile's products; then wait for
-    // the current tile only (the 2*NL newest loads may stay in flight).
+    // wave's next item) goes out before this tile's products. Then wait for
+    // this tile (and, at an item's first tile, its Q rows): everything but the
+    // 2*NL loads just issued and the item-end stores issued before them.
     nxt = cur;
     bool have_next;
     if (cur.tile + 1 < cur.n_tiles) {
@@ -239,14 +242,41 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       have_next = locate(cur.item + nwaves, nxt);
     }
     if (have_next) {
-      issue(nxt, stage ^ 1);
-      wait_vmcnt<2 * NL>();
+      issue_kv(nxt, stage ^ 1);
+      if (stores_out)
+        wait_vmcnt<2 * NL + NS>();
+      else
+        wait_vmcnt<2 * NL>();
     } else {
       wait_all_memory();
     }
+    stores_out = false;
+    if (cur.tile == 0) {
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        qf[ds] = *reinterpret_cast<const u32x4_t*>(qslot + qop + ds * 16);
+      // The slot is free once these reads are done; the next item's rows
+      // may then be fetched into it.
+      wait_lgkmcnt0();
+    }
+    if (have_next && nxt.tile == 0) issue_q(nxt);
 
     const unsigned char* kt = ring + stage * Lay::kStage;
     const unsigned char* vt = kt + Lay::kTile;
+
+    // V^T operands of both 16-key steps: vtr[4 * db + 2 * ks + h] holds the
+    // rows 8h .. 8h+7 of step ks for column block db (read as one group now,
+    // so that their latency hides behind the K reads).
+    u32x2_t vtr[4 * DB];
+    {
+      uint32_t vbase[DB];
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vbase[db] = lds_addr(vt) + vop[db];
+      if constexpr (DB == 4)
+        lds_read_tr16_x16<8 * ROW>(vtr, vbase);
+      else
+        lds_read_tr16_x8<8 * ROW>(vtr, vbase);
+    }
 
     f32x16_t s = (f32x16_t){};
     const unsigned char* krow = kt + r32 * ROW;
@@ -306,9 +336,8 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const unsigned char* p0 = vt + vop[db] + ks * 16 * ROW;
-        const u32x2_t a_lo = lds_read_tr16(p0);
-        const u32x2_t a_hi = lds_read_tr16(p0 + 8 * ROW);
+        const u32x2_t a_lo = vtr[4 * db + 2 * ks];
+        const u32x2_t a_hi = vtr[4 * db + 2 * ks + 1];
         const u32x4_t a = {a_lo[0], a_lo[1], a_hi[0], a_hi[1]};
         oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
       }
@@ -316,6 +345,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
     if (cur.tile + 1 == cur.n_tiles) {
       // End of the item: O_c = O^T / l_rounded, LSE_c = ln2 * (m + log2 l).
+      // Exactly NS vector-memory stores (lanes 0 and 32 always take part).
       const float l_row = sum_with_partner32(l_part);
       const float lr_row = sum_with_partner32(lr_part);
       if (r32 < R) {
@@ -335,7 +365,12 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         if (half == 0)
           part_lse[row * C + cur.c] = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
       }
-      if (have_next) begin_item(nxt);
+      stores_out = true;
+      m_used = -INFINITY;
+      l_part = 0.f;
+      lr_part = 0.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
     }
     // This wave's reads of the stage must be complete before the loads of the
     // tile after next are issued into it.

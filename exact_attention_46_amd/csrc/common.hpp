@@ -104,13 +104,19 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// Cache-policy bits of a buffer load: 0 is the default; kNonTemporal marks a
+// stream read once (the data need not stay in the caches).
+constexpr int kCacheDefault = 0;
+constexpr int kNonTemporal = 2;
+
 // 16-byte load from a raw buffer straight into LDS: lane p's 16 bytes land at
 // lds_base + 16 * p (lds_base must be the same for the whole wave); offsets
 // past the buffer end write zeros. Completion is counted by vmcnt.
+template <int Policy = kCacheDefault>
 __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds_base,
                                                uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, 0);
+      r, (__attribute__((address_space(3))) void*)lds_base, 16, off, 0, 0, Policy);
 }
 
 typedef __attribute__((ext_vector_type(4))) short s16x4_t;
@@ -123,6 +129,68 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4_t*)(p));
   return __builtin_bit_cast(u32x2_t, v);
+}
+
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Four groups of four transposing LDS reads (ds_read_b64_tr_b16, lane layout
+// as in lds_read_tr16): out[4 * j + i] is read at LDS address base[j] + i * STEP.
+// The group ends by waiting for all of this wave's LDS accesses, so the results
+// are valid when it returns. It is written in assembly because the compiler
+// cannot tell these reads apart from the buffer loads to LDS still in flight
+// (which target other LDS bytes) and would otherwise make them wait for every
+// outstanding vector-memory load first.
+template <int STEP>
+__device__ __forceinline__ void lds_read_tr16_x16(u32x2_t (&out)[16], const uint32_t (&base)[4]) {
+  static_assert(3 * STEP < 65536, "ds offset field is 16 bits");
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %16\n\t"
+      "ds_read_b64_tr_b16 %1, %16 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %2, %16 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %3, %16 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %4, %17\n\t"
+      "ds_read_b64_tr_b16 %5, %17 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %6, %17 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %7, %17 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %8, %18\n\t"
+      "ds_read_b64_tr_b16 %9, %18 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %10, %18 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %11, %18 offset:%22\n\t"
+      "ds_read_b64_tr_b16 %12, %19\n\t"
+      "ds_read_b64_tr_b16 %13, %19 offset:%20\n\t"
+      "ds_read_b64_tr_b16 %14, %19 offset:%21\n\t"
+      "ds_read_b64_tr_b16 %15, %19 offset:%22\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
+        "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7]), "=&v"(out[8]), "=&v"(out[9]),
+        "=&v"(out[10]), "=&v"(out[11]), "=&v"(out[12]), "=&v"(out[13]), "=&v"(out[14]),
+        "=&v"(out[15])
+      : "v"(base[0]), "v"(base[1]), "v"(base[2]), "v"(base[3]), "i"(STEP), "i"(2 * STEP),
+        "i"(3 * STEP)
+      : "memory");
+}
+
+// Two groups of four transposing LDS reads, as lds_read_tr16_x16.
+template <int STEP>
+__device__ __forceinline__ void lds_read_tr16_x8(u32x2_t (&out)[8], const uint32_t (&base)[2]) {
+  static_assert(3 * STEP < 65536, "ds offset field is 16 bits");
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b16 %4, %9\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:%10\n\t"
+      "ds_read_b64_tr_b16 %6, %9 offset:%11\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:%12\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), "=&v"(out[4]),
+        "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7])
+      : "v"(base[0]), "v"(base[1]), "i"(STEP), "i"(2 * STEP), "i"(3 * STEP)
+      : "memory");
 }
 
 // Waits for every outstanding memory operation of this wave (vector memory,
