@@ -46,7 +46,75 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="restrict the timed step (for per-kernel profiles)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run a plain streaming kernel of known size "
+                         "(the calibration of HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "'bench.py --copy-calibration' into " + TRAFFIC_FILE)
     return ap.parse_args()
+
+
+COPY_CAL_BYTES = 256 << 20  # bytes read (and written) by one calibration launch
+COPY_CAL_MATCH = "neg"      # the calibration kernel's name contains this
+
+
+def copy_calibration(torch, dev):
+    """Three launches of a plain elementwise kernel that reads COPY_CAL_BYTES and
+    writes as many (y = -x over bf16)."""
+    x = torch.ones(COPY_CAL_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+
+
+def _counter_means(folder, counter):
+    """Mean value per dispatch of `counter`, by kernel name, over every
+    *counter_collection.csv under `folder`."""
+    import csv
+    import glob
+    vals = {}
+    files = glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % folder)
+    for fn in files:
+        with open(fn) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def record_traffic(fetch_dir, write_dir):
+    """HBM bytes per launch of the timed kernels: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each divided by what the same counter reads per byte of the
+    calibration kernel."""
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        hits = [v for k, v in table.items() if key in k]
+        if len(hits) != 1:
+            raise SystemExit("expected one kernel matching %r, found %d" % (key, len(hits)))
+        return hits[0]
+
+    f_cal = pick(fetch, COPY_CAL_MATCH) * 1024.0 / COPY_CAL_BYTES
+    w_cal = pick(write, COPY_CAL_MATCH) * 1024.0 / COPY_CAL_BYTES
+    rec = {"_calibration": {"kernel": "torch.neg over %d bytes of bf16" % COPY_CAL_BYTES,
+                            "fetch_counter_bytes_per_byte": round(f_cal, 4),
+                            "write_counter_bytes_per_byte": round(w_cal, 4)}}
+    for name, match in (("attn_fwd_kernel/llm_prefill", "attn_fwd_kernel"),
+                        ("attn_decode_split_kernel/decode", "attn_decode_split_kernel")):
+        fb = pick(fetch, match) * 1024.0 / f_cal
+        wb = pick(write, match) * 1024.0 / w_cal
+        rec[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                     "bytes_per_launch": round(fb + wb), "source_hash": source_hash()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec, indent=1))
 
 
 def source_hash():
@@ -107,6 +175,9 @@ def cpu_baseline(w, q, k, v, target_s):
 
 def main():
     args = parse()
+    if args.record_traffic:
+        record_traffic(*args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -173,6 +244,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     print("bench: timed %d steps in %.3f s" % (args.steps, wall), file=sys.stderr, flush=True)
+
+    if args.copy_calibration:
+        copy_calibration(torch, dev)
 
     fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     split_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))

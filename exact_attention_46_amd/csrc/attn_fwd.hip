@@ -78,14 +78,26 @@ __device__ __forceinline__ int v_swz(int row) {
   return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
 }
 
-// Maps the linear workgroup id to (batch*head unit, query tile). Heaviest causal
-// tiles first; when the units split evenly over the 8 XCDs (workgroups are
-// dispatched round-robin over XCDs) every XCD gets a contiguous block of units,
-// whole GQA groups included, so K/V reuse stays inside one L2.
+// Maps the linear workgroup id to (batch*head unit, query tile). Workgroups are
+// dispatched round-robin over the 8 XCDs, each with its own L2. When the units
+// split evenly, every XCD gets a contiguous block of units (whole GQA groups
+// included) and walks it kFwdL2Units units at a time, all query tiles of those
+// units before the next ones, heaviest causal tiles first within them: the
+// workgroups resident on an XCD then share the K/V of a few heads, which stay
+// in its L2.
+constexpr int kFwdL2Units = 8;
+
 __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group, int causal,
                                             int& unit, int& qtile) {
+  constexpr int G = kFwdL2Units;
   int rank;
-  if (units % 8 == 0 && (units / 8) % group == 0) {
+  if (units % 8 == 0 && (units / 8) % G == 0 && G % group == 0) {
+    const int upx = units / 8;
+    const int x = L % 8, s = L / 8;
+    const int grp = s / (G * nqt), r = s % (G * nqt);
+    rank = r / G;
+    unit = x * upx + grp * G + r % G;
+  } else if (units % 8 == 0 && (units / 8) % group == 0) {
     const int upx = units / 8;
     const int x = L % 8, s = L / 8;
     rank = s / upx;
