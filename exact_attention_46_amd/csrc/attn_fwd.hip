@@ -5,9 +5,9 @@
 // "flash_attention_forward.cu" page).
 //
 // Work decomposition
-//   one workgroup = 4 waves = 128 query rows of one (batch, head); each wave owns
+//   one workgroup = 8 waves = 256 query rows of one (batch, head); each wave owns
 //   32 query rows for the whole pass. K/V tiles of 64 keys stream through LDS
-//   (two K and two V buffers) and are shared by the 4 waves.
+//   (two K and two V buffers) and are shared by the 8 waves.
 //
 // Per wave and K/V tile (both products on 32x32x16 MFMA, fp32 accumulate):
 //   S^T[64 keys x 32 rows] = K_tile * Q_w^T      A = K from LDS, B = Q^T in VGPRs
@@ -38,19 +38,26 @@
 // reads; V^T operands come from two ds_read_b64_tr_b16 per MFMA, whose
 // 16-lane transpose turns row-major V into the key-major A-operand layout.
 //
-// Software pipeline. Iteration t issues S(t+1) = K(t+1) Q^T before the softmax
-// of S(t) and O += V(t) P(t), so the next tile's products do not wait for this
-// tile's softmax. K runs two tiles ahead of V: iteration t loads K(t+2) into
-// the buffer K(t) occupied and V(t+1) into the buffer of V(t-1); one barrier
-// per iteration publishes both.
+// Two-phase schedule. The two waves that share a SIMD (waves w and w + 4) take
+// opposite roles: while one issues its matrix products the other runs its
+// softmax on the vector ALU, and a barrier between the phases swaps them. An
+// exponential issued by the same wave between its own MFMAs stalls the matrix
+// pipe (measured on gfx950), while one from the partner wave does not. Per
+// tile t, wave group A does [S(t+1) = K(t+1) Q^T, O += P(t) V(t)] | barrier |
+// [softmax of S(t+1)], group B does [softmax of S(t)] | barrier |
+// [S(t+1), O += P(t) V(t)]; in both orders the rescale of O for a tile follows
+// the P V of the tile before it. Iteration t also loads K(t+2) and V(t+1) (into
+// the buffers K(t) and V(t-1) left) and ends with a barrier that publishes
+// them.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace mi355attn {
 
-constexpr int kFwdBM = 128;     // query rows per workgroup
+constexpr int kFwdBM = 256;     // query rows per workgroup
 constexpr int kFwdBN = 64;      // keys per K/V tile
-constexpr int kFwdThreads = 256;
+constexpr int kFwdWaves = 8;
+constexpr int kFwdThreads = 64 * kFwdWaves;
 constexpr float kTau = 8.0f;    // lazy-rescale threshold, log2 units
 
 template <int D>
@@ -58,9 +65,11 @@ struct FwdLayout {
   static constexpr int kRow = D * 2;                 // bytes per row
   static constexpr int kChunks = D / 8;              // 16-byte chunks per row
   static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one wave load covers
-  static constexpr int kLoadsPerWave = kFwdBN / kRowsPerLoad / 4;  // per tensor
+  static constexpr int kLoadsPerWave = kFwdBN / kRowsPerLoad / kFwdWaves;  // per tensor
   static constexpr int kTile = kFwdBN * kRow;        // bytes of one K or V tile
-  static constexpr int kLds = 4 * kTile;             // two K and two V buffers
+  static constexpr int kQWave = 32 * kRow;           // one wave's Q rows
+  static constexpr int kQLoads = 32 / kRowsPerLoad;  // loads per wave for them
+  static constexpr int kLds = 4 * kTile + kFwdWaves * kQWave;  // K, V (two each), Q
 };
 
 // Chunk swizzles (chunk index XOR f(row)), chosen against the LDS bank layout
@@ -110,7 +119,7 @@ __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group
 }
 
 template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kFwdThreads, 2)
+__global__ void __launch_bounds__(kFwdThreads, 1)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                 float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
@@ -138,7 +147,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   const int off = Nk - Nq;  // bottom-right causal alignment
   const int q0 = qtile * kFwdBM;
-  const int qw0 = q0 + wave * 32;  // first query row of this wave
+  // Role and rows: waves w and w + 4 share a SIMD; w < 4 is group A, the
+  // others group B. The partners own adjacent 32-row blocks, so their causal
+  // work is nearly equal.
+  const int role_b = wave >> 2;
+  const int qw0 = q0 + (2 * (wave & 3) + role_b) * 32;  // first query row of this wave
   const int my_row = qw0 + r32;
 
   const uint16_t* qh = q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
@@ -154,12 +167,20 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
   const int n_tiles = (kv_end + kFwdBN - 1) / kFwdBN;
 
-  // ---- Q^T operand: lane holds row my_row, d-chunk (half * DS + ds) for step ds
-  // (rows past Nq read as zero).
-  u32x4_t qf[DS];
+  // ---- Q: the wave's 32 rows go HBM -> its own LDS block once, swizzled like
+  // K (rows past Nq land as zeros); the Q^T operand of each product is read
+  // from there (lane: row r32, d-chunk half * DS + ds), which keeps the
+  // registers for the accumulators.
+  unsigned char* qslot = smem + 4 * Lay::kTile + wave * Lay::kQWave;
+  auto issue_q = [&]() {
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
-    qf[ds] = buf_load16(rq, (uint32_t)my_row * ROW + (half * DS + ds) * 16);
+    for (int i = 0; i < Lay::kQLoads; ++i) {
+      const int row = i * Lay::kRowsPerLoad + lane / Lay::kChunks;
+      const int pc = lane % Lay::kChunks;
+      const uint32_t src = (uint32_t)(qw0 + row) * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
+      buf_load16_lds(rq, qslot + i * 1024, src);
+    }
+  };
 
   // ---- tile loads: load i of wave w covers tile rows (w*LPW + i)*RPL ..
   // +RPL-1; lane p fills physical chunk p % C of row p / C, i.e. it loads
@@ -224,30 +245,59 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const bool wave_rows_valid = qw0 < Nq;
   const int wave_last_row = min(qw0 + 31, Nq - 1);
 
-  // Tile t is active for this wave when some row of the wave may see key 64t.
-  auto active = [&](int t) {
-    return wave_rows_valid && (!CAUSAL || t * kFwdBN <= wave_last_row + off);
+  u32x4_t qf[DS];  // Q^T operands, read from the wave's LDS block after the prologue
+
+  // Operand reads run a few products ahead of the MFMAs that use them, in a
+  // fixed order (each step is closed by a scheduling barrier), so that an
+  // MFMA finds its operands in registers instead of waiting for LDS.
+  constexpr int KA = 3;  // K steps read ahead
+  constexpr int VA = 3;  // V^T products read ahead
+  const unsigned char* vbase_t;  // V tile of the P V being prefetched
+  u32x2_t vlo[VA + 1], vhi[VA + 1];
+  // V^T operand of product i of P V (step ks = i / DB, column block db = i % DB).
+  auto read_v = [&](int i) {
+    const int ks = i / DB, db = i % DB, slot = i % (VA + 1);
+    const unsigned char* p0 = vbase_t + vop[db] + ks * 16 * ROW;
+    vlo[slot] = lds_read_tr16_staged((const lds_s16x4_t*)p0);
+    vhi[slot] = lds_read_tr16_staged((const lds_s16x4_t*)(p0 + 8 * ROW));
   };
 
-  // S^T(t) = K(t) * Q^T for two 32-key blocks.
-  auto qk = [&](int t, f32x16_t* s) {
+  // S^T(t) = K(t) * Q^T for two 32-key blocks; with_v: the first V^T operands
+  // of the P V of tile tv are read during the last steps.
+  auto qk = [&](int t, f32x16_t* s, bool with_v, int tv) {
     const unsigned char* kt = kbuf + (t & 1) * Lay::kTile;
+    vbase_t = vbuf + (tv & 1) * Lay::kTile;
+    s[0] = (f32x16_t){};
+    s[1] = (f32x16_t){};
+    u32x4_t ka[KA], kb[KA];
+    auto read_k = [&](int ds) {
+      const int chunk = ((half * DS + ds) ^ kx) << 4;
+      ka[ds % KA] = *reinterpret_cast<const u32x4_t*>(kt + r32 * ROW + chunk);
+      kb[ds % KA] = *reinterpret_cast<const u32x4_t*>(kt + (32 + r32) * ROW + chunk);
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16_t){};
-      const unsigned char* krow = kt + (kb * 32 + r32) * ROW;
+    for (int ds = 0; ds < KA; ++ds) read_k(ds);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        u32x4_t a = *reinterpret_cast<const u32x4_t*>(krow + (((half * DS + ds) ^ kx) << 4));
-        s[kb] = mfma32x32x16<DT>(a, qf[ds], s[kb]);
+    for (int ds = 0; ds < DS; ++ds) {
+      s[0] = mfma32x32x16<DT>(ka[ds % KA], qf[ds], s[0]);
+      s[1] = mfma32x32x16<DT>(kb[ds % KA], qf[ds], s[1]);
+      if (ds + KA < DS) {
+        read_k(ds + KA);
+      } else if (with_v) {
+        const int i = ds + KA - DS;  // 0 .. KA-1
+        if (i < VA) read_v(i);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Softmax of S^T(t) into the P^T operands, then O^T += V(t)^T * P^T.
-  auto softmax_pv = [&](int t, f32x16_t* s) {
+  // Masks S^T(t), takes its row maximum and moves the exponent offset m
+  // (rescaling O and the sums) when the maximum outgrew it; then
+  // P^T = exp2(s * c - m) into the 16-bit B operands pf (the row sum uses the
+  // unrounded values, the second sum the rounded ones).
+  auto softmax = [&](int t, f32x16_t* s, u32x4_t* pf) {
     const int k0 = t * kFwdBN;
-    const unsigned char* vt = vbuf + (t & 1) * Lay::kTile;
     // Mask keys past the end and (causal) keys after the row's limit.
     // Element e of block kb holds key k0 + 32*kb + 4*half + 8*(e/4) + e%4.
     const bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
@@ -261,12 +311,17 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
 
-    // Row maximum of this tile (raw scores; scale > 0 keeps the order).
-    float mx = s[0][0];
+    // Row maximum of this tile (raw scores; scale > 0 keeps the order), as a
+    // tree: independent chains keep the vector pipeline busy.
+    float mq[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+    for (int j = 0; j < 4; ++j) {
+      const f32x16_t& x = s[j >> 1];
+      const int e0 = 8 * (j & 1);
+      mq[j] = fmaxf(fmaxf(fmaxf(x[e0], x[e0 + 1]), fmaxf(x[e0 + 2], x[e0 + 3])),
+                    fmaxf(fmaxf(x[e0 + 4], x[e0 + 5]), fmaxf(x[e0 + 6], x[e0 + 7])));
+    }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = max_with_partner32(mx);
     const float m_tile = mx * c;
 
@@ -284,16 +339,15 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     const float neg_m = (m_used == -INFINITY) ? 0.f : -m_used;
 
-    // P^T = exp2(s * c - m); the row sum uses the unrounded values.
-    u32x4_t pf[4];
-    float lsum = 0.f;
+    // Both row sums in four independent partial sums each.
+    float ls[4] = {0.f, 0.f, 0.f, 0.f}, lrs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         p[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, neg_m));
-        lsum += p[e];
+        ls[e & 3] += p[e];
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -301,60 +355,110 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                    pack2<DT>(p[8 * j + 2], p[8 * j + 3]),
                                    pack2<DT>(p[8 * j + 4], p[8 * j + 5]),
                                    pack2<DT>(p[8 * j + 6], p[8 * j + 7])};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lrs[w] = add_pair<DT>(pf[kb * 2 + j][w], lrs[w]);
       }
     }
-    l_part += lsum;
-    float lrsum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) lrsum = add_pair<DT>(pf[j][w], lrsum);
-    lr_part += lrsum;
+    l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    lr_part += (lrs[0] + lrs[1]) + (lrs[2] + lrs[3]);
+  };
 
-    // O^T += V^T * P^T. For step ks the lane-half `half` needs, in k-slot m,
-    // key 16*ks + 8*(m/4) + 4*half + m%4: the first transposing read gives
-    // slots 0..3 (rows 16*ks + 4*half + 0..3), the second slots 4..7 (8 rows
-    // further).
+  // O^T += V(t)^T * P^T. For step ks the lane-half `half` needs, in k-slot m,
+  // key 16*ks + 8*(m/4) + 4*half + m%4: the first transposing read gives slots
+  // 0..3 (rows 16*ks + 4*half + 0..3), the second slots 4..7 (8 rows further).
+  // prefetched: the first VA products' operands were read during S^T.
+  auto pv = [&](int t, const u32x4_t* pf, bool prefetched) {
+    vbase_t = vbuf + (t & 1) * Lay::kTile;
+    constexpr int NP = 4 * DB;
+    if (!prefetched) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int i = 0; i < VA; ++i) read_v(i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const unsigned char* p0 = vt + vop[db] + ks * 16 * ROW;
-        const u32x2_t lo = lds_read_tr16(p0);
-        const u32x2_t hi = lds_read_tr16(p0 + 8 * ROW);
-        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma32x32x16<DT>(a, pf[ks], oacc[db]);
-      }
+    for (int i = 0; i < NP; ++i) {
+      const int slot = i % (VA + 1);
+      if (i + VA < NP) read_v(i + VA);
+      const u32x4_t a = {vlo[slot][0], vlo[slot][1], vhi[slot][0], vhi[slot][1]};
+      oacc[i % DB] = mfma32x32x16<DT>(a, pf[i / DB], oacc[i % DB]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // Prologue: K(0), V(0), K(1) in flight; S(0) once they land.
-  f32x16_t sa[2], sb[2];
+  // Tiles active for this wave (some row may see key 64t) form a prefix.
+  int n_act = 0;
+  if (wave_rows_valid) {
+    n_act = n_tiles;
+    if (CAUSAL) {
+      const int last_key = wave_last_row + off;  // keys up to here are visible
+      n_act = last_key < 0 ? 0 : min(n_tiles, last_key / kFwdBN + 1);
+    }
+  }
+
+  // Prologue: K(0), V(0), K(1) and the wave's Q rows in flight; S(0) once they
+  // land; group A also takes the softmax of S(0). The barrier after that frees
+  // K(0)'s buffer. Each group then runs its own copy of the loop (one code path
+  // per role keeps the register allocation of each to what that role needs);
+  // both pass the same barriers.
+  f32x16_t st[2];  // S of the next tile to take through the softmax
+  u32x4_t pf[4];   // P of the next tile to multiply with V
   if (n_tiles > 0) {
     issue_k(0);
     issue_v(0);
   }
   if (n_tiles > 1) issue_k(1);
+  issue_q();
   wait_all_memory();
   __syncthreads();
-  if (n_tiles > 0 && active(0)) qk(0, sa);
-
-  // One iteration: loads for t+2 (K) and t+1 (V), S(t+1), the softmax and P V
-  // of tile t, then the barrier that publishes the loads.
-  auto step = [&](int t, f32x16_t* s_cur, f32x16_t* s_next) {
+  // Q^T operand in registers: lane holds row r32, d-chunk half * DS + ds.
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+    qf[ds] = *reinterpret_cast<const u32x4_t*>(qslot + r32 * ROW + (((half * DS + ds) ^ kx) << 4));
+  auto loads = [&](int t) {
     if (t + 2 < n_tiles) issue_k(t + 2);
     if (t + 1 < n_tiles) issue_v(t + 1);
-    if (t + 1 < n_tiles && active(t + 1)) qk(t + 1, s_next);
-    if (active(t)) softmax_pv(t, s_cur);
-    wait_all_memory();
-    __syncthreads();
   };
-  int t = 0;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+  // The barrier between the two phases only keeps the partners in step; no
+  // data crosses it, so it carries no memory fence (a fence would wait for the
+  // tile loads still in flight).
+  auto phase_barrier = []() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The matrix phase of tile t: S(t+1) when tile t+1 is active, P V of tile t
+  // when tile t is.
+  auto matrix_phase = [&](int t) {
+    const bool act = t < n_act, act_next = t + 1 < n_act;
+    if (act_next) qk(t + 1, st, act, t);
+    if (act) pv(t, pf, act_next);
+  };
+  if (!role_b) {
+    if (n_act > 0) {
+      qk(0, st, false, 0);
+      softmax(0, st, pf);
+    }
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      loads(t);
+      matrix_phase(t);
+      phase_barrier();
+      if (t + 1 < n_act) softmax(t + 1, st, pf);
+      wait_all_memory();
+      __syncthreads();
+    }
+  } else {
+    if (n_act > 0) qk(0, st, false, 0);
+    __syncthreads();
+    for (int t = 0; t < n_tiles; ++t) {
+      loads(t);
+      if (t < n_act) softmax(t, st, pf);
+      phase_barrier();
+      matrix_phase(t);
+      wait_all_memory();
+      __syncthreads();
+    }
   }
-  if (t < n_tiles) step(t, sa, sb);
 
   // ---- epilogue: O = O^T / l_rounded, LSE = ln2 * (m + log2 l).
   const float l_row = sum_with_partner32(l_part);

@@ -131,6 +131,20 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// The same transposing read for kernels that stage tiles with buffer loads to
+// LDS. The compiler's wait insertion treats an LDS read that carries no alias
+// scope as possibly reading bytes a buffer load to LDS still in flight writes,
+// and precedes it with a wait for all outstanding vector-memory loads. The
+// restrict-qualified parameter gives the read a scope of its own, which lifts
+// that wait; the caller guarantees (with its own waits and barriers) that the
+// bytes it reads have landed.
+__device__ __forceinline__ u32x2_t lds_read_tr16_staged(const lds_s16x4_t* __restrict__ p) {
+  return __builtin_bit_cast(u32x2_t,
+                            __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p)));
+}
+
 // 32-bit LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
