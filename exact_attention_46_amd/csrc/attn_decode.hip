@@ -22,8 +22,11 @@
 // the wave. No wave ever waits for another, and a wave waits only for the
 // tile it is about to use: vector-memory operations of a wave complete in
 // issue order, so "at most N outstanding" with N = the loads issued after the
-// tile (plus the partial-result stores issued after it at an item end) means
-// the tile has landed.
+// tile (plus the partial-result stores issued after it) means the tile has
+// landed. Because completion is in order, a store also holds back every load
+// issued after it until it is acknowledged; an item's output therefore waits
+// in registers and is stored one iteration later, right after that
+// iteration's wait, which gives the stores two tiles' time.
 //
 // Per tile: S^T[32 keys x 32 cols] = K Q^T (8 MFMAs 32x32x16), the running
 // max / sum update of the online softmax (the OnlineSoftmaxState of the
@@ -226,7 +229,32 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     issue_q(cur);
   }
   int stage = 0;
-  bool stores_out = false;  // the previous tile ended an item (its stores are in flight)
+  bool stores_out = false;  // the previous iteration issued an item's stores
+  // An item's output waits in registers for one iteration and is stored after
+  // the next tile's loads have landed (see the header).
+  bool pend = false;
+  f32x16_t opend[DB];
+  float* pend_dst = part_o;
+  float* pend_lse = part_lse;
+  float pend_lse_val = 0.f;
+  // Exactly NS vector-memory stores (lanes 0 and 32 always take part).
+  auto store_pending = [&]() {
+    if (r32 < R) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int d0 = db * 32 + 8 * gq + 4 * half;
+          // The combine reads the partials once, later: stream them past
+          // the caches instead of holding KV lines' space for them.
+          __builtin_nontemporal_store((f32x4_t){opend[db][4 * gq + 0], opend[db][4 * gq + 1],
+                                                opend[db][4 * gq + 2], opend[db][4 * gq + 3]},
+                                      reinterpret_cast<f32x4_t*>(pend_dst + d0));
+        }
+      if (half == 0) __builtin_nontemporal_store(pend_lse_val, pend_lse);
+    }
+    pend = false;
+  };
 
   while (have) {
     // The next position (next tile of this item, or the first tile of the
@@ -251,6 +279,10 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       wait_all_memory();
     }
     stores_out = false;
+    if (pend) {  // younger than the loads waited for above
+      store_pending();
+      stores_out = true;
+    }
     if (cur.tile == 0) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
@@ -344,28 +376,20 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     }
 
     if (cur.tile + 1 == cur.n_tiles) {
-      // End of the item: O_c = O^T / l_rounded, LSE_c = ln2 * (m + log2 l).
-      // Exactly NS vector-memory stores (lanes 0 and 32 always take part).
+      // End of the item: O_c = O^T / l_rounded, LSE_c = ln2 * (m + log2 l),
+      // held until the next iteration (at most one item's output is pending:
+      // it was stored at the top of this iteration).
       const float l_row = sum_with_partner32(l_part);
       const float lr_row = sum_with_partner32(lr_part);
-      if (r32 < R) {
-        const int64_t row = (int64_t)cur.b * Hq + (int64_t)cur.g * R + r32;
-        const bool empty = !(l_row > 0.f);
-        const float inv = empty ? 0.f : 1.f / lr_row;
-        float* dst = part_o + (row * C + cur.c) * D;
+      const int64_t row = (int64_t)cur.b * Hq + (int64_t)cur.g * R + (r32 < R ? r32 : 0);
+      const bool empty = !(l_row > 0.f);
+      const float inv = empty ? 0.f : 1.f / lr_row;
+      pend_dst = part_o + (row * C + cur.c) * D;
+      pend_lse = part_lse + row * C + cur.c;
+      pend_lse_val = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int d0 = db * 32 + 8 * gq + 4 * half;
-            *reinterpret_cast<f32x4_t*>(dst + d0) =
-                (f32x4_t){oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv,
-                          oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv};
-          }
-        if (half == 0)
-          part_lse[row * C + cur.c] = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
-      }
-      stores_out = true;
+      for (int db = 0; db < DB; ++db) opend[db] = oacc[db] * inv;
+      pend = true;
       m_used = -INFINITY;
       l_part = 0.f;
       lr_part = 0.f;
@@ -380,6 +404,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     have = have_next;
     stage ^= 1;
   }
+  if (pend) store_pending();
 }
 
 template <int DT, int D>
