@@ -311,18 +311,18 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       }
     }
 
-    // Row maximum of this tile (raw scores; scale > 0 keeps the order), as a
-    // tree: independent chains keep the vector pipeline busy.
-    float mq[4];
+    // Row maximum of this tile (raw scores; scale > 0 keeps the order): one
+    // chain of three-way maxima per 32-key block, two new values per step.
+    float mb[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const f32x16_t& x = s[j >> 1];
-      const int e0 = 8 * (j & 1);
-      mq[j] = fmaxf(fmaxf(fmaxf(x[e0], x[e0 + 1]), fmaxf(x[e0 + 2], x[e0 + 3])),
-                    fmaxf(fmaxf(x[e0 + 4], x[e0 + 5]), fmaxf(x[e0 + 6], x[e0 + 7])));
+    for (int kb = 0; kb < 2; ++kb) {
+      const f32x16_t& x = s[kb];
+      float r = fmaxf(fmaxf(x[0], x[1]), x[2]);
+#pragma unroll
+      for (int e = 3; e + 1 < 16; e += 2) r = fmaxf(fmaxf(r, x[e]), x[e + 1]);
+      mb[kb] = fmaxf(r, x[15]);
     }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mx = max_with_partner32(mx);
+    float mx = max_with_partner32(fmaxf(mb[0], mb[1]));
     const float m_tile = mx * c;
 
     const bool grow = m_tile > m_used + kTau;
@@ -339,15 +339,19 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
     const float neg_m = (m_used == -INFINITY) ? 0.f : -m_used;
 
-    // Both row sums in four independent partial sums each.
-    float ls[4] = {0.f, 0.f, 0.f, 0.f}, lrs[4] = {0.f, 0.f, 0.f, 0.f};
+    // Both row sums in four independent partial sums each (the unrounded
+    // ones start from the first four values).
+    float ls[4], lrs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         p[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, neg_m));
-        ls[e & 3] += p[e];
+        if (kb == 0 && e < 4)
+          ls[e] = p[e];
+        else
+          ls[e & 3] += p[e];
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
