@@ -48,7 +48,9 @@
 // [S(t+1), O += P(t) V(t)]; in both orders the rescale of O for a tile follows
 // the P V of the tile before it. Iteration t also loads K(t+2) and V(t+1) (into
 // the buffers K(t) and V(t-1) left) and ends with a barrier that publishes
-// them.
+// them. Each product runs as one dependent MFMA chain per accumulator block
+// (all steps of S block 0, then block 1; all key steps of each O block), 2-3%
+// faster on gfx950 than interleaving the blocks.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -250,13 +252,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // Operand reads run a few products ahead of the MFMAs that use them, in a
   // fixed order (each step is closed by a scheduling barrier), so that an
   // MFMA finds its operands in registers instead of waiting for LDS.
-  constexpr int KA = 3;  // K steps read ahead
   constexpr int VA = 3;  // V^T products read ahead
   const unsigned char* vbase_t;  // V tile of the P V being prefetched
   u32x2_t vlo[VA + 1], vhi[VA + 1];
-  // V^T operand of product i of P V (step ks = i / DB, column block db = i % DB).
+  // V^T operand of product i of P V (column block db = i / 4, step ks = i % 4).
   auto read_v = [&](int i) {
-    const int ks = i / DB, db = i % DB, slot = i % (VA + 1);
+    const int ks = i % 4, db = i / 4, slot = i % (VA + 1);
     const unsigned char* p0 = vbase_t + vop[db] + ks * 16 * ROW;
     vlo[slot] = lds_read_tr16_staged((const lds_s16x4_t*)p0);
     vhi[slot] = lds_read_tr16_staged((const lds_s16x4_t*)(p0 + 8 * ROW));
@@ -269,23 +270,25 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     vbase_t = vbuf + (tv & 1) * Lay::kTile;
     s[0] = (f32x16_t){};
     s[1] = (f32x16_t){};
-    u32x4_t ka[KA], kb[KA];
-    auto read_k = [&](int ds) {
+    constexpr int KR = 4;  // K operand reads ahead
+    u32x4_t kr[KR];
+    // product j: key block kb = j / DS, step ds = j % DS
+    auto read_k = [&](int j) {
+      const int kb = j / DS, ds = j % DS;
       const int chunk = ((half * DS + ds) ^ kx) << 4;
-      ka[ds % KA] = *reinterpret_cast<const u32x4_t*>(kt + r32 * ROW + chunk);
-      kb[ds % KA] = *reinterpret_cast<const u32x4_t*>(kt + (32 + r32) * ROW + chunk);
+      kr[j % KR] = *reinterpret_cast<const u32x4_t*>(kt + (32 * kb + r32) * ROW + chunk);
     };
 #pragma unroll
-    for (int ds = 0; ds < KA; ++ds) read_k(ds);
+    for (int j = 0; j < KR; ++j) read_k(j);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      s[0] = mfma32x32x16<DT>(ka[ds % KA], qf[ds], s[0]);
-      s[1] = mfma32x32x16<DT>(kb[ds % KA], qf[ds], s[1]);
-      if (ds + KA < DS) {
-        read_k(ds + KA);
+    for (int j = 0; j < 2 * DS; ++j) {
+      const int kb = j / DS, ds = j % DS;
+      s[kb] = mfma32x32x16<DT>(kr[j % KR], qf[ds], s[kb]);
+      if (j + KR < 2 * DS) {
+        read_k(j + KR);
       } else if (with_v) {
-        const int i = ds + KA - DS;  // 0 .. KA-1
+        const int i = j + KR - 2 * DS;  // 0 .. KR-1
         if (i < VA) read_v(i);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -384,7 +387,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       const int slot = i % (VA + 1);
       if (i + VA < NP) read_v(i + VA);
       const u32x4_t a = {vlo[slot][0], vlo[slot][1], vhi[slot][0], vhi[slot][1]};
-      oacc[i % DB] = mfma32x32x16<DT>(a, pf[i / DB], oacc[i % DB]);
+      oacc[i / 4] = mfma32x32x16<DT>(a, pf[i % 4], oacc[i / 4]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
