@@ -470,24 +470,40 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // ---- epilogue: O = O^T / l_rounded, LSE = ln2 * (m + log2 l).
   const float l_row = sum_with_partner32(l_part);
   const float lr_row = sum_with_partner32(lr_part);
-  if (my_row < Nq) {
-    const bool empty = !(l_row > 0.f);
-    const float inv = empty ? 0.f : 1.f / lr_row;
-    uint16_t* orow = o + (((int64_t)b * Hq + h) * (int64_t)Nq + my_row) * D;
+  const bool empty = !(l_row > 0.f);
+  const float inv = empty ? 0.f : 1.f / lr_row;
+  // O^T (lane: row r32, d = 32 db + 8 gq + 4 half + 0..3) goes row-major
+  // through the wave's Q block in LDS (free since the prologue; 32 rows x ROW
+  // bytes), 16-byte chunk c of row r stored at chunk c ^ (r mod chunks per
+  // row) so that neither side has bank conflicts; the rows then leave in
+  // whole-row stores of 16 bytes per lane (4 rows per store at d = 128), not
+  // written through the caches. Scattered 8-byte stores straight from the
+  // accumulators cost 4% of the kernel on gfx950.
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPS = 64 / CPR;  // rows per store
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+  for (int db = 0; db < DB; ++db) {
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d0 = db * 32 + 8 * gq + 4 * half;
-        u32x2_t w = {pack2<DT>(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
-                     pack2<DT>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(orow + d0) = w;
-      }
+    for (int gq = 0; gq < 4; ++gq) {
+      u32x2_t w = {pack2<DT>(oacc[db][4 * gq + 0] * inv, oacc[db][4 * gq + 1] * inv),
+                   pack2<DT>(oacc[db][4 * gq + 2] * inv, oacc[db][4 * gq + 3] * inv)};
+      const int chunk = (4 * db + gq) ^ (r32 & (CPR - 1));
+      *reinterpret_cast<u32x2_t*>(qslot + r32 * ROW + chunk * 16 + half * 8) = w;
     }
-    if (half == 0) {
-      float out = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
-      lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
-    }
+  }
+  wait_lgkmcnt0();
+  uint16_t* otile = o + (((int64_t)b * Hq + h) * (int64_t)Nq + qw0) * D;
+  const int cl = lane % CPR, rl = lane / CPR;
+#pragma unroll
+  for (int s0 = 0; s0 < 32; s0 += RPS) {
+    const int r = s0 + rl;
+    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(qslot + r * ROW + ((cl ^ (r & (CPR - 1))) << 4));
+    if (qw0 + r < Nq)
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(otile + (int64_t)r * D + cl * 8));
+  }
+  if (my_row < Nq && half == 0) {
+    const float out = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
+    lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
   }
 }
 
