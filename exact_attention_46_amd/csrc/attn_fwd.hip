@@ -434,11 +434,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     __builtin_amdgcn_sched_barrier(0);
   };
   // The matrix phase of tile t: S(t+1) when tile t+1 is active, P V of tile t
-  // when tile t is.
+  // when tile t is. The wave raises its issue priority for it, so that when
+  // both waves of a SIMD have an instruction ready the next MFMA of the chain
+  // goes first and the softmax of the partner fills the cycles in between
+  // (1.5-2% faster on gfx950 across causal and non-causal shapes).
   auto matrix_phase = [&](int t) {
     const bool act = t < n_act, act_next = t + 1 < n_act;
+    __builtin_amdgcn_s_setprio(1);
     if (act_next) qk(t + 1, st, act, t);
     if (act) pv(t, pf, act_next);
+    __builtin_amdgcn_s_setprio(0);
   };
   if (!role_b) {
     if (n_act > 0) {
