@@ -10,6 +10,8 @@ every timed step.
 Prints ONE JSON line:
   value       prefill TFLOP/s = 4*B*H*N*N*d/2 / mean forward kernel time
   decode      KV GB/s = sum_b 2*Hkv*L_b*d*2 bytes / mean (split + combine) time
+  decode_paged  the same decode over a paged cache (64-row pages, shuffled pool,
+                block tables), timed in a loop of its own after the steps
   roofline    the forward kernel against the bf16 dense MFMA peak
   cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the prefill
                 workload, in the same TFLOP/s unit
@@ -44,6 +46,8 @@ def parse():
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-cache decode measurement")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="restrict the timed step (for per-kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -106,7 +110,10 @@ def record_traffic(fetch_dir, write_dir):
                             "fetch_counter_bytes_per_byte": round(f_cal, 4),
                             "write_counter_bytes_per_byte": round(w_cal, 4)}}
     for name, match in (("attn_fwd_kernel/llm_prefill", "attn_fwd_kernel"),
-                        ("attn_decode_split_kernel/decode", "attn_decode_split_kernel")):
+                        ("attn_decode_split_kernel/decode",
+                         "attn_decode_split_kernel<0, 128, false>"),
+                        ("attn_decode_split_kernel/decode_paged",
+                         "attn_decode_split_kernel<0, 128, true>")):
         fb = pick(fetch, match) * 1024.0 / f_cal
         wb = pick(write, match) * 1024.0 / w_cal
         rec[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
@@ -171,6 +178,50 @@ def cpu_baseline(w, q, k, v, target_s):
             "sample": "%d seeded random query rows of the llm_prefill workload (exact fp64 "
                       "causal rows, avg %d keys), %.1f s" % (n, int(rows[:, 2].mean()) + 1, dt),
             "seconds": dt}
+
+
+PAGE_SIZE = 64
+
+
+def bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream):
+    """The decode workload laid out in PAGE_SIZE-row pages of a shuffled pool
+    (block table per sequence): split-KV decode over the paged cache, timed like
+    the contiguous one but outside the step."""
+    print("bench: paged decode (page %d)" % PAGE_SIZE, file=sys.stderr, flush=True)
+    kp, vp, table = wl.paged_from_padded(kc, vc, sl, PAGE_SIZE, seed=wd.seed)
+    td = table.to(kc.device)
+    bufs = ea.decode_buffers(dq, table.shape[1] * PAGE_SIZE, wd.chunk)
+
+    def run(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ea.attn_decode_split_paged(dq, kp, vp, td, sld, bufs[0], bufs[1], wd.chunk, wd.scale,
+                                   stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ea.attn_decode_combine(bufs[0], bufs[1], sld, bufs[2], bufs[3], wd.chunk, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        run(events[i])
+    torch.cuda.synchronize()
+    split_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    lens = sl.numpy().astype(np.int64)
+    kv_bytes = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
+    gbs = kv_bytes / ((split_ms + comb_ms) * 1e-3) / 1e9
+    del kp, vp
+    return {"value": round(gbs, 1), "unit": "GB/s", "page_size": PAGE_SIZE,
+            "split_ms": round(split_ms, 4), "combine_ms": round(comb_ms, 4),
+            "roofline": {"kernel": "attn_decode_split_kernel<bf16,128,paged>", "bound": "hbm",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("attn_decode_split_kernel/decode_paged")}}
 
 
 def main():
@@ -294,6 +345,9 @@ def main():
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("attn_decode_split_kernel/decode")}}
+    if do_dec and not args.no_paged:
+        out["decode_paged"] = bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc,
+                                          stream)
     if not args.no_cpu_baseline and do_pre:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wp, q, k, v, args.cpu_seconds)

@@ -1,4 +1,5 @@
-"""MI355X-native exact attention: fused forward with LSE and split-KV decode.
+"""MI355X-native exact attention: fused forward with LSE and split-KV decode
+(contiguous or paged KV cache).
 
 The compute runs in hand-written HIP kernels for gfx950 behind a C ABI
 (``include/mi355attn.h``, built into ``libmi355attn.so``); this package is the
@@ -11,10 +12,12 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attn_decode_combine,
     attn_decode_split,
+    attn_decode_split_paged,
     attn_fwd,
     attn_status_str,
     decode,
     decode_buffers,
+    decode_paged,
     default_scale,
     fwd,
     load_library,

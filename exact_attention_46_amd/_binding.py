@@ -27,7 +27,8 @@ ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
 
-EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_combine", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_split_paged", "attn_decode_combine",
+           "attn_status_str")
 
 _DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 
@@ -51,10 +52,13 @@ def load_library() -> ctypes.CDLL:
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
+        lib.attn_decode_split_paged.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f,
+                                                i, p]
         lib.attn_decode_combine.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p]
         lib.attn_status_str.argtypes = [i]
         lib.attn_fwd.restype = i
         lib.attn_decode_split.restype = i
+        lib.attn_decode_split_paged.restype = i
         lib.attn_decode_combine.restype = i
         lib.attn_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -135,6 +139,32 @@ def attn_decode_split(q, k_cache, v_cache, seq_lens, part_o, part_lse, chunk: in
         raise AttnError("attn_decode_split", st)
 
 
+def attn_decode_split_paged(q, k_pages, v_pages, block_table, seq_lens, part_o, part_lse,
+                            chunk: int, scale: float, stream=None) -> None:
+    """Calls attn_decode_split_paged. q [B,Hq,d]; pages [num_pages,page_size,Hkv,d];
+    block_table [B,max_pages] int32; part_o [B,Hq,C,d], part_lse [B,Hq,C] fp32 with
+    C = ceil(max_pages*page_size/chunk)."""
+    _gpu(q, k_pages, v_pages, block_table, seq_lens, part_o, part_lse)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pages.shape
+    _need(v_pages.shape == k_pages.shape and k_pages.shape[3] == d, "page shapes")
+    _need(k_pages.dtype == q.dtype and v_pages.dtype == q.dtype, "dtypes differ")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
+          block_table.shape[0] == B, "block_table [B,max_pages] int32")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens [B] int32")
+    max_pages = block_table.shape[1]
+    C = -(-(max_pages * page_size) // chunk)
+    _need(part_o.dtype == torch.float32 and tuple(part_o.shape) == (B, Hq, C, d), "part_o shape")
+    _need(part_lse.dtype == torch.float32 and tuple(part_lse.shape) == (B, Hq, C),
+          "part_lse shape")
+    st = load_library().attn_decode_split_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(part_o),
+        _ptr(part_lse), B, Hq, Hkv, num_pages, page_size, max_pages, d, int(chunk), float(scale),
+        _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode_split_paged", st)
+
+
 def attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk: int, stream=None) -> None:
     """Calls attn_decode_combine. o [B,Hq,d] bf16/fp16, lse [B,Hq] fp32."""
     _gpu(part_o, part_lse, seq_lens, o, lse)
@@ -179,5 +209,19 @@ def decode(q, k_cache, v_cache, seq_lens, chunk: int = 512, scale: float | None 
         buffers = decode_buffers(q, k_cache.shape[2], chunk)
     part_o, part_lse, o, lse = buffers
     attn_decode_split(q, k_cache, v_cache, seq_lens, part_o, part_lse, chunk, scale, stream)
+    attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk, stream)
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, chunk: int = 512,
+                 scale: float | None = None, stream=None, buffers=None):
+    """Split-KV decode over a paged cache: split then combine. Returns (o, lse)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    if buffers is None:
+        buffers = decode_buffers(q, block_table.shape[1] * k_pages.shape[1], chunk)
+    part_o, part_lse, o, lse = buffers
+    attn_decode_split_paged(q, k_pages, v_pages, block_table, seq_lens, part_o, part_lse, chunk,
+                            scale, stream)
     attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk, stream)
     return o, lse

@@ -61,6 +61,39 @@ extern "C" int attn_decode_split(const void* q, const void* k_cache, const void*
   return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int attn_decode_split_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       const int* block_table, const int* seq_lens,
+                                       float* part_o, float* part_lse, int B, int Hq, int Hkv,
+                                       int num_pages, int page_size, int max_pages, int d,
+                                       int chunk, float scale, int dtype, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !seq_lens || !part_o || !part_lse)
+    return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || num_pages <= 0 || page_size <= 0 || max_pages <= 0 ||
+      d <= 0 || chunk <= 0)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || (int64_t)max_pages * page_size > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype) || Hq / Hkv > 32) return MI355ATTN_ERR_UNSUPPORTED;
+  // Every 1 KiB load of a tile (4 rows at d = 128, 8 at d = 64, starting at a
+  // multiple of that count when chunk and page_size are multiples of 16) stays
+  // inside one page, and the chunk of a work item may span at most 16 pages.
+  const int item_pages = chunk % page_size == 0 ? chunk / page_size
+                                                : (chunk + page_size - 2) / page_size + 1;
+  if (page_size % 16 != 0 || chunk % 16 != 0 || item_pages > 16)
+    return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k_pages, 16) || !aligned(v_pages, 16) || !aligned(part_o, 16) ||
+      !aligned(part_lse, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  const int max_len = max_pages * page_size;
+  if (mi355attn::split_work_items(B, Hkv, max_len, chunk) > kMaxGrid ||
+      (int64_t)B * Hq * (((int64_t)max_len + chunk - 1) / chunk) > ((int64_t)1 << 40) ||
+      (int64_t)B * max_pages > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::SplitArgs a{q, k_pages, v_pages, seq_lens, part_o, part_lse, B, Hq, Hkv, max_len,
+                         d, chunk, scale, dtype, block_table, page_size, max_pages, num_pages};
+  return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_decode_combine(const float* part_o, const float* part_lse,
                                    const int* seq_lens, void* o, float* lse, int B, int Hq,
                                    int max_chunks, int d, int chunk, int dtype, void* stream) {

@@ -100,12 +100,24 @@ __device__ __forceinline__ int total_chunks(const int* seq_lens, int B, int max_
   return t;
 }
 
-template <int DT, int D>
+// Paged caches: the chunk of one work item spans at most this many pages (the
+// C ABI checks it), whose physical numbers the wave keeps in scalar registers.
+constexpr int kMaxItemPages = 16;
+
+// Where the keys of a sequence live. Contiguous: [B, Hkv, max_len, d]. Paged:
+// [num_pages, page_size, Hkv, d] with block_table [B, max_pages]; logical key j
+// of sequence b is row j % page_size of page block_table[b][j / page_size].
+struct PagedKV {
+  const int* block_table;
+  int page_size, max_pages, num_pages;
+};
+
+template <int DT, int D, bool PAGED>
 __global__ void __launch_bounds__(kSplitThreads, 1)
 attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                          const uint16_t* __restrict__ vc, const int* __restrict__ seq_lens,
                          float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq,
-                         int Hkv, int max_len, int chunk, int C, float scale) {
+                         int Hkv, int max_len, int chunk, int C, float scale, PagedKV pk) {
   using Lay = SplitLayout<D>;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
@@ -139,13 +151,17 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // DMA offsets of this lane inside a tile (relative to the tile's first row):
   // load i covers rows i*RPL .. +RPL-1; lane p fills physical chunk p % C of
   // row p / C, i.e. loads logical chunk (p % C) ^ swz(row).
+  // Paged caches: each load gets a buffer resource of its own, based at its
+  // first row inside its page; lane offsets then step by the page row stride.
+  const uint32_t pstride = PAGED ? (uint32_t)Hkv * ROW : (uint32_t)ROW;  // bytes between rows
   uint32_t koff[NL], voff[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int row = i * Lay::kRowsPerLoad + lane / Lay::kChunks;
     const int pc = lane % Lay::kChunks;
-    koff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ dk_swz<D>(row)) * 16);
-    voff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ dv_swz<D>(row)) * 16);
+    const uint32_t rbase = PAGED ? (uint32_t)(lane / Lay::kChunks) * pstride : (uint32_t)row * ROW;
+    koff[i] = rbase + (uint32_t)((pc ^ dk_swz<D>(row)) * 16);
+    voff[i] = rbase + (uint32_t)((pc ^ dv_swz<D>(row)) * 16);
   }
   // Operand read offsets, as in the forward kernel.
   const int kx = dk_swz<D>(r32);
@@ -172,6 +188,8 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // A work position: item, tile inside the item, and the item's geometry.
   struct Pos {
     int item, tile, b, g, c, L, n_tiles;
+    int lp0;                  // paged: first logical page of the chunk
+    int pg[PAGED ? kMaxItemPages : 1];  // paged: physical pages of the chunk's pages
   };
   auto locate = [&](int item, Pos& p) -> bool {
     p.item = item;
@@ -191,20 +209,52 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     const int lo = p.c * chunk;
     const int hi = min(p.L, lo + chunk);
     p.n_tiles = (hi - lo + kSplitBN - 1) / kSplitBN;
+    if constexpr (PAGED) {
+      // Scalar loads of the block-table entries of this chunk (indices clamped
+      // into the sequence's row of the table; entries past the chunk are
+      // never used).
+      p.lp0 = lo / pk.page_size;
+      const int* row = pk.block_table + (int64_t)p.b * pk.max_pages;
+#pragma unroll
+      for (int k = 0; k < kMaxItemPages; ++k) p.pg[k] = row[min(p.lp0 + k, pk.max_pages - 1)];
+    }
     return true;
   };
   auto issue_kv = [&](const Pos& p, int stage) {
     const int r0 = p.c * chunk + p.tile * kSplitBN;  // < L for every issued tile
-    const int64_t head = ((int64_t)p.b * Hkv + p.g) * (int64_t)max_len + r0;
-    const uint32_t valid = (uint32_t)(p.L - r0) * ROW;  // rows past L read as zero
-    const auto rk = make_rsrc(kc + head * D, valid);
-    const auto rv = make_rsrc(vc + head * D, valid);
     unsigned char* kt = ring + stage * Lay::kStage;
     unsigned char* vt = kt + Lay::kTile;
+    if constexpr (PAGED) {
+      // Load i covers logical rows r0 + i*RPL .. +RPL-1, all inside one page
+      // (RPL divides the page size). Rows at or past L, and pages outside
+      // [0, num_pages), read as zeros.
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      buf_load16_lds<kNonTemporal>(rk, kt + i * 1024, koff[i]);
-      buf_load16_lds<kNonTemporal>(rv, vt + i * 1024, voff[i]);
+      for (int i = 0; i < NL; ++i) {
+        const int ri = r0 + i * Lay::kRowsPerLoad;
+        const int lp = ri / pk.page_size;
+        int phys = p.pg[0];
+#pragma unroll
+        for (int k = 1; k < kMaxItemPages; ++k) phys = (lp - p.lp0 == k) ? p.pg[k] : phys;
+        int rows = min(p.L - ri, Lay::kRowsPerLoad);
+        if (phys < 0 || phys >= pk.num_pages) rows = 0;
+        if (rows < 0) rows = 0;
+        const int64_t base =
+            (((int64_t)(rows > 0 ? phys : 0) * pk.page_size + (ri - lp * pk.page_size)) * Hkv +
+             p.g) * (int64_t)D;
+        const uint32_t bytes = rows > 0 ? (uint32_t)(rows - 1) * pstride + ROW : 0u;
+        buf_load16_lds<kNonTemporal>(make_rsrc(kc + base, bytes), kt + i * 1024, koff[i]);
+        buf_load16_lds<kNonTemporal>(make_rsrc(vc + base, bytes), vt + i * 1024, voff[i]);
+      }
+    } else {
+      const int64_t head = ((int64_t)p.b * Hkv + p.g) * (int64_t)max_len + r0;
+      const uint32_t valid = (uint32_t)(p.L - r0) * ROW;  // rows past L read as zero
+      const auto rk = make_rsrc(kc + head * D, valid);
+      const auto rv = make_rsrc(vc + head * D, valid);
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        buf_load16_lds<kNonTemporal>(rk, kt + i * 1024, koff[i]);
+        buf_load16_lds<kNonTemporal>(rv, vt + i * 1024, voff[i]);
+      }
     }
   };
   // The R query rows of item p (contiguous in q) into the Q slot, row-major.
@@ -502,11 +552,20 @@ static int device_cus() {
 
 template <int DT, int D>
 static hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
-  const int C = (int)(((int64_t)a.max_len + a.chunk - 1) / a.chunk);
-  hipLaunchKernelGGL((attn_decode_split_kernel<DT, D>), dim3((unsigned)device_cus()),
-                     dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
-                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens, a.part_o,
-                     a.part_lse, a.B, a.Hq, a.Hkv, a.max_len, a.chunk, C, a.scale);
+  const int max_len = a.block_table ? a.max_pages * a.page_size : a.max_len;
+  const int C = (int)(((int64_t)max_len + a.chunk - 1) / a.chunk);
+  const PagedKV pk{a.block_table, a.page_size, a.max_pages, a.num_pages};
+  if (a.block_table) {
+    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, true>), dim3((unsigned)device_cus()),
+                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk);
+  } else {
+    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false>), dim3((unsigned)device_cus()),
+                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk);
+  }
   return hipGetLastError();
 }
 

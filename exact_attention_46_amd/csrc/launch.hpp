@@ -28,6 +28,10 @@ struct SplitArgs {
   int B, Hq, Hkv, max_len, d, chunk;
   float scale;
   int dtype;
+  // Paged caches (block_table != nullptr): k_cache / v_cache are
+  // [num_pages, page_size, Hkv, d] and max_len is max_pages * page_size.
+  const int* block_table = nullptr;
+  int page_size = 0, max_pages = 0, num_pages = 0;
 };
 
 struct CombineArgs {

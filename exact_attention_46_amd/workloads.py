@@ -16,7 +16,12 @@ Recipe (all draws from ``torch.Generator`` seeded with the workload's seed):
     any read past the end of a sequence shows up in the output. The cache draws
     use a generator on the device the cache lives on (a 4 GiB cache is too slow to
     draw on the host), so the values differ between a CPU and a GPU cache; the
-    lengths and q never do.
+    lengths and q never do;
+  * paged decode: the rows of a padded decode cache are laid out in pages of
+    ``page_size`` rows ([num_pages, page_size, Hkv, d]) at the positions of a
+    seeded ``randperm`` of the pool, plus ``spare`` unused pages; every row no
+    sequence uses (unused pages, the tail of each sequence's last page) is NaN,
+    and unused block-table slots hold -1.
 """
 from __future__ import annotations
 
@@ -150,3 +155,33 @@ def workload_decode_inputs(w: Workload, device="cpu"):
 def bits(t: torch.Tensor):
     """Raw 16-bit patterns of a bf16/fp16 tensor as a numpy uint16 array (CPU copy)."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def paged_from_padded(k_cache, v_cache, seq_lens, page_size, seed=0, spare=3):
+    """Lays a padded cache [B,Hkv,max_len,d] out in a shuffled page pool.
+
+    Returns (k_pages, v_pages [num_pages,page_size,Hkv,d], block_table [B,max_pages]
+    int32 on the CPU). Sequence b's logical page p (rows p*page_size ..) goes to
+    pool page block_table[b][p]; pages are assigned by a seeded permutation so
+    neighbouring logical pages are scattered."""
+    B, Hkv, max_len, d = k_cache.shape
+    lens = [int(x) for x in torch.as_tensor(seq_lens)]
+    max_pages = -(-max_len // page_size)
+    need = [-(-L // page_size) for L in lens]
+    num_pages = sum(need) + spare
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    perm = torch.randperm(num_pages, generator=g).tolist()
+    dev = k_cache.device
+    kp = torch.full((num_pages, page_size, Hkv, d), float("nan"), dtype=k_cache.dtype, device=dev)
+    vp = torch.full_like(kp, float("nan"))
+    table = torch.full((B, max_pages), -1, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        for p in range(need[b]):
+            pg = perm[nxt]
+            nxt += 1
+            table[b, p] = pg
+            r0, r1 = p * page_size, min(lens[b], (p + 1) * page_size)
+            kp[pg, : r1 - r0] = k_cache[b, :, r0:r1].transpose(0, 1)
+            vp[pg, : r1 - r0] = v_cache[b, :, r0:r1].transpose(0, 1)
+    return kp, vp, table

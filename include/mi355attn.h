@@ -97,6 +97,39 @@ int attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
                       void* stream);
 
 /*
+ * attn_decode_split_paged — attn_decode_split over a paged KV cache (block
+ * tables), the cache layout of the aprender-gpu page's
+ * "attention/paged/flash_decoding" module: the keys of a sequence live in
+ * fixed-size pages anywhere in a shared pool, and a per-sequence table lists
+ * the pages in order.
+ *
+ *   q           [B, Hq, d]                         dtype  (read)
+ *   k_pages     [num_pages, page_size, Hkv, d]     dtype  (read: rows a sequence uses)
+ *   v_pages     [num_pages, page_size, Hkv, d]     dtype  (read: rows a sequence uses)
+ *   block_table [B, max_pages]                     int32, device memory (read)
+ *   seq_lens    [B]                                int32, device memory (read); values
+ *                                                  clamped to [0, max_pages * page_size]
+ *   part_o      [B, Hq, C, d]                      float  (written as in attn_decode_split)
+ *   part_lse    [B, Hq, C]                         float  (written as in attn_decode_split)
+ *
+ * with C = ceil(max_pages * page_size / chunk). Logical key j of sequence b is
+ * row j % page_size of page block_table[b][j / page_size]; pages may be shared
+ * between sequences (read only). The result is that of attn_decode_split on the
+ * cache these lookups describe, and attn_decode_combine (with max_chunks = C)
+ * merges it. page_size and chunk must be multiples of 16 and one chunk may span
+ * at most 16 pages (chunk / page_size <= 16 when chunk is a multiple of
+ * page_size, else (chunk + page_size - 2) / page_size + 1 <= 16), else
+ * MI355ATTN_ERR_UNSUPPORTED.
+ * Table entries a sequence uses must lie in [0, num_pages); the kernel never
+ * reads outside k_pages / v_pages: an entry out of range reads as zero keys
+ * and values (the result for that sequence is then meaningless).
+ */
+int attn_decode_split_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int* block_table, const int* seq_lens, float* part_o,
+                            float* part_lse, int B, int Hq, int Hkv, int num_pages, int page_size,
+                            int max_pages, int d, int chunk, float scale, int dtype, void* stream);
+
+/*
  * attn_decode_combine — second half of split-KV decode: merges the partials of
  * each (b, h) with the rescaling combine (the two passes of the aprender-gpu
  * reduce kernel: global maximum M of the chunk LSEs, then weights

@@ -50,11 +50,13 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, i64, p, p, i]
         lib.oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, f, p, p, i]
+        lib.oracle_decode_paged.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_decode_chunks.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_combine.argtypes = [p, p, p, i, i, i, i, i, p, p]
         lib.oracle_decode_values.argtypes = [p, i64, i, p]
         lib.oracle_max_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_decode,
+                   lib.oracle_decode_paged,
                    lib.oracle_decode_chunks, lib.oracle_combine, lib.oracle_decode_values,
                    lib.oracle_max_threads):
             fn.restype = ctypes.c_int
@@ -132,6 +134,26 @@ def decode(q, k_cache, v_cache, seq_lens, dtype: int, scale: float, nthreads: in
     rc = _load().oracle_decode(_ptr(q), _ptr(kc), _ptr(vc), _ptr(sl), dtype, B, Hq, Hkv,
                                max_len, d, float(scale), _ptr(o), _ptr(lse), nthreads)
     _check(rc, "decode")
+    return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, dtype: int, scale: float,
+                 nthreads: int = 0):
+    """Single-token decode over a paged cache: q [B,Hq,d], pages [num_pages,page_size,Hkv,d],
+    block_table [B,max_pages] int32 -> (o [B,Hq,d], lse [B,Hq])."""
+    q, kp, vp = _u16(q), _u16(k_pages), _u16(v_pages)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    sl = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = kp.shape
+    if vp.shape != kp.shape or dk != d or bt.ndim != 2 or bt.shape[0] != B:
+        raise ValueError("shape mismatch")
+    o = np.empty((B, Hq, d), dtype=np.float64)
+    lse = np.empty((B, Hq), dtype=np.float64)
+    rc = _load().oracle_decode_paged(_ptr(q), _ptr(kp), _ptr(vp), _ptr(bt), _ptr(sl), dtype, B,
+                                     Hq, Hkv, num_pages, page_size, bt.shape[1], d,
+                                     float(scale), _ptr(o), _ptr(lse), nthreads)
+    _check(rc, "decode_paged")
     return o, lse
 
 

@@ -270,6 +270,67 @@ int oracle_decode(const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_
 }
 
 /*
+ * Single-token decode against a paged KV cache (the layout of the aprender-gpu
+ * page's "attention/paged/flash_decoding" module: fixed-size pages in a shared
+ * pool, and a per-sequence table listing them in order).
+ *   q [B,Hq,d]; k_pages, v_pages [num_pages, page_size, Hkv, d];
+ *   block_table [B, max_pages]; seq_lens [B]
+ *   o [B,Hq,d] fp64; lse [B,Hq] fp64
+ * Key j of sequence b is row j % page_size of page block_table[b][j / page_size]
+ * (kv-head g within that row). Each (b, h) first gathers its L_b key and value
+ * rows through the table into contiguous scratch, then attends to them exactly
+ * as oracle_decode does. A table entry that a sequence uses outside
+ * [0, num_pages) is a bad argument.
+ */
+int oracle_decode_paged(const uint16_t* q, const uint16_t* k_pages, const uint16_t* v_pages,
+                        const int32_t* block_table, const int32_t* seq_lens, int dtype, int B,
+                        int Hq, int Hkv, int num_pages, int page_size, int max_pages, int d,
+                        float scale, double* o, double* lse, int nthreads) {
+    if (num_pages <= 0 || page_size <= 0 || max_pages <= 0) return -1;
+    const int64_t max_len = (int64_t)max_pages * page_size;
+    if (max_len > 0x7fffffff) return -1;
+    if (check_decode(B, Hq, Hkv, (int)max_len, d, dtype, seq_lens)) return -1;
+    for (int b = 0; b < B; ++b)
+        for (int64_t j = 0; j < seq_lens[b]; j += page_size) {
+            const int32_t pg = block_table[(int64_t)b * max_pages + j / page_size];
+            if (pg < 0 || pg >= num_pages) return -1;
+        }
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t nrows = (int64_t)B * Hq;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)max_len);
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* vrow = (double*)malloc(sizeof(double) * (size_t)d);
+        uint16_t* kg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)max_len * (size_t)d);
+        uint16_t* vg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)max_len * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t b = r / Hq, h = r % Hq;
+            int64_t g = h * Hkv / Hq;
+            const int64_t L = seq_lens[b];
+            /* 1. gather the sequence's rows of kv-head g through the block table */
+            for (int64_t j = 0; j < L; ++j) {
+                const int64_t pg = block_table[b * max_pages + j / page_size];
+                const int64_t src = ((pg * page_size + j % page_size) * Hkv + g) * (int64_t)d;
+                memcpy(kg + j * d, k_pages + src, sizeof(uint16_t) * (size_t)d);
+                memcpy(vg + j * d, v_pages + src, sizeof(uint16_t) * (size_t)d);
+            }
+            /* 2. the plain decode row over the gathered keys */
+            decode_vec(q + r * (int64_t)d, d, dtype, qrow);
+            attend_row(qrow, kg, vg, dtype, 0, L, d, sc, s, vrow, o + r * (int64_t)d, lse + r);
+        }
+        free(s);
+        free(qrow);
+        free(vrow);
+        free(kg);
+        free(vg);
+    }
+    return 0;
+}
+
+/*
  * Split-KV partials: for every (b, h, c) with C = ceil(max_len / chunk) chunk
  * slots, the exact attention of the query over keys
  * [c*chunk, min((c+1)*chunk, seq_lens[b])), normalised within the chunk.

@@ -101,6 +101,25 @@ def test_attn_decode_split_rejects(lib, kw, code):
     assert split(lib, **kw) == code
 
 
+def split_paged(lib, q=A, kp=A, vp=A, bt=A2, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2,
+                num_pages=10, page_size=32, max_pages=4, d=128, chunk=64, scale=0.1, dtype=0):
+    return lib.attn_decode_split_paged(q, kp, vp, bt, sl, po, pl, B, Hq, Hkv, num_pages,
+                                       page_size, max_pages, d, chunk, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(kp=None), -1), (dict(bt=None), -1), (dict(pl=None), -1),
+    (dict(B=0), -2), (dict(num_pages=0), -2), (dict(page_size=0), -2), (dict(max_pages=0), -2),
+    (dict(chunk=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(max_pages=2**18, page_size=64), -2),
+    (dict(d=80), -3), (dict(dtype=7), -3), (dict(Hq=66, Hkv=2), -3),
+    (dict(page_size=24), -3), (dict(chunk=40), -3), (dict(page_size=16, chunk=512), -3),
+    (dict(page_size=48, chunk=800), -3),
+    (dict(scale=float("nan")), -5), (dict(vp=MIS), -4), (dict(bt=ctypes.c_void_p(4098)), -4),
+])
+def test_attn_decode_split_paged_rejects(lib, kw, code):
+    assert split_paged(lib, **kw) == code
+
+
 def combine(lib, po=A, pl=A2, sl=A2, o=A, lse=A2, B=2, Hq=8, C=4, d=128, chunk=16, dtype=0):
     return lib.attn_decode_combine(po, pl, sl, o, lse, B, Hq, C, d, chunk, dtype, None)
 

@@ -354,6 +354,64 @@ def test_combine_two_chunks_closed_form():
     assert abs(lse[0, 0] - math.log(4.0)) < 1e-15
 
 
+@pytest.mark.parametrize("page_size", [16, 32, 48, 512])
+def test_paged_decode_equals_decode_of_the_logical_cache(page_size):
+    """A paged cache holds the same keys as the padded cache it was scattered
+    from (numpy/torch scatter in the input module, not the oracle), so the paged
+    decode must reproduce the padded decode exactly, and torch's fp64 SDPA on
+    the logical keys."""
+    lens = [0, 1, page_size - 1, page_size, page_size + 1, 3 * page_size + 5, 100]
+    sl, q, kc, vc = wl.decode_inputs(len(lens), 8, 2, 64, "bf16", 21, max_len=max(lens) + 7,
+                                     seq_lens=lens)
+    kp, vp, table = wl.paged_from_padded(kc, vc, sl, page_size, seed=5)
+    ro, rl = oracle.decode(_bits(q), _bits(kc), _bits(vc), sl.numpy(), 0, 0.125)
+    po, pl = oracle.decode_paged(_bits(q), _bits(kp), _bits(vp), table.numpy(), sl.numpy(), 0,
+                                 0.125)
+    assert np.array_equal(ro, po) and np.array_equal(rl, pl)
+    b = 5  # longest sequence: library routine on its logical keys
+    L = lens[b]
+    qt = q[b].double()[:, None, None, :]            # [Hq,1,1,d]
+    kt = kc[b, :, :L].double().repeat_interleave(4, dim=0)[:, None]  # [Hq,1,L,d]
+    vt = vc[b, :, :L].double().repeat_interleave(4, dim=0)[:, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=0.125)
+    assert np.abs(po[b] - ref[:, 0, 0].numpy()).max() < 1e-12
+
+
+def test_paged_decode_with_shared_prefix_pages():
+    """Two sequences whose tables list the same first pages (a shared prompt)
+    see the same keys there: the result equals the padded decode of a cache in
+    which the shared rows are copied into both sequences."""
+    ps, d, Hkv = 32, 64, 2
+    g = torch.Generator().manual_seed(9)
+    pool_k = torch.randn((6, ps, Hkv, d), generator=g).to(torch.bfloat16)
+    pool_v = torch.randn((6, ps, Hkv, d), generator=g).to(torch.bfloat16)
+    q = torch.randn((2, 4, d), generator=g).to(torch.bfloat16)
+    table = torch.tensor([[4, 1, 3], [4, 1, 0]], dtype=torch.int32)
+    lens = torch.tensor([80, 70], dtype=torch.int32)
+    kc = torch.full((2, Hkv, 96, d), float("nan"), dtype=torch.bfloat16)
+    vc = kc.clone()
+    for b in range(2):
+        for j in range(int(lens[b])):
+            pg = int(table[b, j // ps])
+            kc[b, :, j] = pool_k[pg, j % ps]
+            vc[b, :, j] = pool_v[pg, j % ps]
+    ro, rl = oracle.decode(_bits(q), _bits(kc), _bits(vc), lens.numpy(), 0, 0.125)
+    po, pl = oracle.decode_paged(_bits(q), _bits(pool_k), _bits(pool_v), table.numpy(),
+                                 lens.numpy(), 0, 0.125)
+    assert np.array_equal(ro, po) and np.array_equal(rl, pl)
+
+
+def test_paged_decode_rejects_out_of_range_pages_and_ignores_unused_slots():
+    sl, q, kc, vc = wl.decode_inputs(2, 4, 2, 64, "bf16", 3, max_len=64, seq_lens=[40, 17])
+    kp, vp, table = wl.paged_from_padded(kc, vc, sl, 16, seed=1)
+    t = table.numpy().copy()
+    assert (t[1, 2:] == -1).all()  # unused slots hold -1 and are never looked up
+    oracle.decode_paged(_bits(q), _bits(kp), _bits(vp), t, sl.numpy(), 0, 0.125)
+    t[0, 1] = kp.shape[0]
+    with pytest.raises(ValueError):
+        oracle.decode_paged(_bits(q), _bits(kp), _bits(vp), t, sl.numpy(), 0, 0.125)
+
+
 def test_oracle_rejects_bad_arguments():
     q = np.zeros((1, 3, 4, 8), dtype=np.uint16)
     k = np.zeros((1, 2, 4, 8), dtype=np.uint16)
