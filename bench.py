@@ -10,6 +10,8 @@ every timed step.
 Prints ONE JSON line:
   value       prefill TFLOP/s = 4*B*H*N*N*d/2 / mean forward kernel time
   decode      KV GB/s = sum_b 2*Hkv*L_b*d*2 bytes / mean (split + combine) time
+  fwd_varlen    a packed causal prefill batch (8192 tokens in sequences of seeded
+                lengths U[256, 4096]), TFLOP/s, timed in a loop of its own
   decode_paged  the same decode over a paged cache (64-row pages, shuffled pool,
                 block tables), timed in a loop of its own after the steps
   roofline    the forward kernel against the bf16 dense MFMA peak
@@ -46,6 +48,8 @@ def parse():
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed variable-length prefill measurement")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
@@ -181,6 +185,42 @@ def cpu_baseline(w, q, k, v, target_s):
 
 
 PAGE_SIZE = 64
+VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX = 8192, 256, 4096
+
+
+def bench_varlen(args, torch, np, ea, wl, dev, stream):
+    """A packed causal prefill batch with the llm_prefill token budget (8192 tokens,
+    Hq = Hkv = 32, d = 128, bf16) split into sequences of seeded lengths
+    U[256, 4096]; TFLOP/s with the metric's convention, 4*H*N_b^2*d/2 per
+    sequence. Timed in a loop of its own after the steps."""
+    print("bench: packed variable-length prefill", file=sys.stderr, flush=True)
+    lens = wl.varlen_lengths(VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX, seed=1)
+    q, k, v, cq, ck = wl.varlen_inputs(lens, lens, 32, 32, 128, "bf16", seed=1)
+    q, k, v, cq, ck = (t.to(dev) for t in (q, k, v, cq, ck))
+    o = torch.empty_like(q)
+    lse = torch.empty((32, q.shape[0]), dtype=torch.float32, device=dev)
+    scale = 1.0 / 128 ** 0.5
+
+    def run():
+        ea.attn_fwd_varlen(q, k, v, o, lse, cq, ck, max(lens), True, scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    flops = float(sum(4.0 * 32 * n * n * 128 / 2.0 for n in lens))
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "seq_lens": lens,
+            "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal,varlen>", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
 def bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream):
@@ -345,6 +385,8 @@ def main():
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("attn_decode_split_kernel/decode")}}
+    if do_pre and not args.no_varlen:
+        out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
     if do_dec and not args.no_paged:
         out["decode_paged"] = bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc,
                                           stream)

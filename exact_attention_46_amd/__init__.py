@@ -1,5 +1,5 @@
-"""MI355X-native exact attention: fused forward with LSE and split-KV decode
-(contiguous or paged KV cache).
+"""MI355X-native exact attention: fused forward with LSE (dense or packed
+variable-length batches) and split-KV decode (contiguous or paged KV cache).
 
 The compute runs in hand-written HIP kernels for gfx950 behind a C ABI
 (``include/mi355attn.h``, built into ``libmi355attn.so``); this package is the
@@ -14,11 +14,13 @@ from ._binding import (  # noqa: F401
     attn_decode_split,
     attn_decode_split_paged,
     attn_fwd,
+    attn_fwd_varlen,
     attn_status_str,
     decode,
     decode_buffers,
     decode_paged,
     default_scale,
     fwd,
+    fwd_varlen,
     load_library,
 )

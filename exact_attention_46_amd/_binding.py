@@ -27,8 +27,8 @@ ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
 
-EXPORTS = ("attn_fwd", "attn_decode_split", "attn_decode_split_paged", "attn_decode_combine",
-           "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_split", "attn_decode_split_paged",
+           "attn_decode_combine", "attn_status_str")
 
 _DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 
@@ -51,12 +51,14 @@ def load_library() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
+        lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
         lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
         lib.attn_decode_split_paged.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f,
                                                 i, p]
         lib.attn_decode_combine.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p]
         lib.attn_status_str.argtypes = [i]
         lib.attn_fwd.restype = i
+        lib.attn_fwd_varlen.restype = i
         lib.attn_decode_split.restype = i
         lib.attn_decode_split_paged.restype = i
         lib.attn_decode_combine.restype = i
@@ -114,6 +116,30 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                                  _stream(stream))
     if st != OK:
         raise AttnError("attn_fwd", st)
+
+
+def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                    causal: bool, scale: float, stream=None) -> None:
+    """Calls attn_fwd_varlen. q/o [total_q,Hq,d], k/v [total_k,Hkv,d], lse [Hq,total_q] fp32,
+    cu_seqlens_q/k [B+1] int32 on the GPU."""
+    _gpu(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k)
+    _need(q.dim() == 3 and k.dim() == 3 and v.shape == k.shape, "q, k, v must be 3-D, k ~ v")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    _need(k.shape[2] == d, "k/v head dim differs from q")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype and o.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape, "o must have q's shape")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (Hq, total_q), "lse [Hq,total_q] fp32")
+    _need(cu_seqlens_q.dtype == torch.int32 and cu_seqlens_k.dtype == torch.int32 and
+          cu_seqlens_q.dim() == 1 and cu_seqlens_q.shape == cu_seqlens_k.shape and
+          cu_seqlens_q.shape[0] >= 2, "cu_seqlens_q/k [B+1] int32")
+    B = cu_seqlens_q.shape[0] - 1
+    st = load_library().attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv,
+                                        total_q, total_k, int(max_seqlen_q), d, float(scale),
+                                        int(bool(causal)), _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_fwd_varlen", st)
 
 
 def attn_decode_split(q, k_cache, v_cache, seq_lens, part_o, part_lse, chunk: int,
@@ -186,6 +212,18 @@ def fwd(q, k, v, causal: bool = True, scale: float | None = None, stream=None):
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     attn_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, causal: bool = True,
+               scale: float | None = None, stream=None):
+    """Allocates and returns (o [total_q,Hq,d], lse [Hq,total_q]) for a packed batch."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+    attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, causal, scale,
+                    stream)
     return o, lse
 
 

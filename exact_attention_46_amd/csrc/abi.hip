@@ -39,6 +39,27 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                               const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
+                               int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
+                               float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !cu_seqlens_q || !cu_seqlens_k) return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q <= 0 || total_k <= 0 || max_seqlen_q <= 0 ||
+      d <= 0)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || max_seqlen_q > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::fwd_grid_blocks(B, Hq, max_seqlen_q) > kMaxGrid || (int64_t)B * Hq > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, max_seqlen_q, d, scale, causal,
+                       dtype, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_decode_split(const void* q, const void* k_cache, const void* v_cache,
                                  const int* seq_lens, float* part_o, float* part_lse, int B,
                                  int Hq, int Hkv, int max_len, int d, int chunk, float scale,

@@ -120,11 +120,25 @@ __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group
   qtile = causal ? (nqt - 1 - rank) : rank;
 }
 
-template <int DT, int D, bool CAUSAL>
+// Packed variable-length batches: sequence b owns token rows
+// [cu_q[b], cu_q[b+1]) of q/o [total_q, Hq, d] and [cu_k[b], cu_k[b+1]) of k/v
+// [total_k, Hkv, d]; lse is [Hq, total_q]. Offsets are clamped into the tensors.
+struct VarLen {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+};
+
+// VARLEN = false: dense [B, H, N, d] tensors of Nq / Nk rows per head.
+// VARLEN = true: packed batches (see VarLen); Nq / Nk are then the largest
+// sequence lengths, which size the grid, and each workgroup takes its
+// sequence's own lengths (workgroups past the end of a sequence exit).
+template <int DT, int D, bool CAUSAL, bool VARLEN>
 __global__ void __launch_bounds__(kFwdThreads, 1)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
-                float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
+                float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
+                VarLen vl) {
   using Lay = FwdLayout<D>;
   constexpr int DS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -146,9 +160,26 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int b = unit / Hq;
   const int h = unit % Hq;
   const int g = h / group;  // == floor(h * Hkv / Hq) since Hq % Hkv == 0
+  const int q0 = qtile * kFwdBM;
+
+  // Row strides (elements) and this sequence's first rows.
+  constexpr int QS_DENSE = D;
+  const int QS = VARLEN ? Hq * D : QS_DENSE;   // q / o
+  const int KS = VARLEN ? Hkv * D : QS_DENSE;  // k / v
+  int64_t q_row0 = 0, k_row0 = 0;
+  if constexpr (VARLEN) {
+    const int qs = min(max(vl.cu_q[b], 0), vl.total_q);
+    const int qe = min(max(vl.cu_q[b + 1], qs), vl.total_q);
+    const int ks = min(max(vl.cu_k[b], 0), vl.total_k);
+    const int ke = min(max(vl.cu_k[b + 1], ks), vl.total_k);
+    q_row0 = qs;
+    k_row0 = ks;
+    Nq = min(qe - qs, Nq);  // rows past the grid's largest length are not computed
+    Nk = ke - ks;
+    if (q0 >= Nq) return;  // the whole workgroup: this sequence is shorter
+  }
 
   const int off = Nk - Nq;  // bottom-right causal alignment
-  const int q0 = qtile * kFwdBM;
   // Role and rows: waves w and w + 4 share a SIMD; w < 4 is group A, the
   // others group B. The partners own adjacent 32-row blocks, so their causal
   // work is nearly equal.
@@ -156,10 +187,14 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int qw0 = q0 + (2 * (wave & 3) + role_b) * 32;  // first query row of this wave
   const int my_row = qw0 + r32;
 
-  const uint16_t* qh = q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
-  const uint16_t* kh = k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
-  const uint16_t* vh = v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
-  const auto rq = make_rsrc(qh, (uint32_t)Nq * ROW);
+  const uint16_t* qh = VARLEN ? q + (q_row0 * Hq + h) * D : q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
+  const uint16_t* kh = VARLEN ? k + (k_row0 * Hkv + g) * D : k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  const uint16_t* vh = VARLEN ? v + (k_row0 * Hkv + g) * D : v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  // Q rows of this workgroup. Dense: the head's rows, addressed from row 0.
+  // Packed: based at row q0, ranging over the rows below Nq (strided rows).
+  const int q_rows = min(kFwdBM, Nq - q0);
+  const auto rq = VARLEN ? make_rsrc(qh + (int64_t)q0 * QS, (uint32_t)(q_rows - 1) * QS * 2 + ROW)
+                         : make_rsrc(qh, (uint32_t)Nq * ROW);
 
   // Keys this workgroup can see: [0, kv_end).
   int kv_end = Nk;
@@ -179,7 +214,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     for (int i = 0; i < Lay::kQLoads; ++i) {
       const int row = i * Lay::kRowsPerLoad + lane / Lay::kChunks;
       const int pc = lane % Lay::kChunks;
-      const uint32_t src = (uint32_t)(qw0 + row) * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
+      const uint32_t src = VARLEN ? (uint32_t)(qw0 - q0 + row) * QS * 2 + (uint32_t)((pc ^ k_swz<D>(row)) * 16)
+                                  : (uint32_t)(qw0 + row) * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
       buf_load16_lds(rq, qslot + i * 1024, src);
     }
   };
@@ -195,22 +231,31 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int i = 0; i < LPW; ++i) {
     const int row = (wave * LPW + i) * RPL + lane / Lay::kChunks;
     const int pc = lane % Lay::kChunks;
-    koff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
-    voff[i] = (uint32_t)row * ROW + (uint32_t)((pc ^ v_swz<D>(row)) * 16);
+    const uint32_t rb = (uint32_t)row * (uint32_t)KS * 2;  // == row * ROW when dense
+    koff[i] = rb + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
+    voff[i] = rb + (uint32_t)((pc ^ v_swz<D>(row)) * 16);
   }
+  // Bytes a tile's buffer resource covers: its rows below Nk (rows past them
+  // read as zeros).
+  auto tile_bytes = [&](int r0) -> uint32_t {
+    if constexpr (VARLEN)
+      return (uint32_t)(min(kFwdBN, Nk - r0) - 1) * (uint32_t)KS * 2 + ROW;
+    else
+      return (uint32_t)(Nk - r0) * ROW;
+  };
   // LDS: K buffers at [0, 2*kTile), V buffers at [2*kTile, 4*kTile).
   unsigned char* kbuf = smem;
   unsigned char* vbuf = smem + 2 * Lay::kTile;
   auto issue_k = [&](int t) {
     const int r0 = t * kFwdBN;  // < Nk for every tile that is issued
-    const auto rk = make_rsrc(kh + (int64_t)r0 * D, (uint32_t)(Nk - r0) * ROW);
+    const auto rk = make_rsrc(kh + (int64_t)r0 * KS, tile_bytes(r0));
     unsigned char* dst = kbuf + (t & 1) * Lay::kTile;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) buf_load16_lds(rk, dst + (wave * LPW + i) * 1024, koff[i]);
   };
   auto issue_v = [&](int t) {
     const int r0 = t * kFwdBN;
-    const auto rv = make_rsrc(vh + (int64_t)r0 * D, (uint32_t)(Nk - r0) * ROW);
+    const auto rv = make_rsrc(vh + (int64_t)r0 * KS, tile_bytes(r0));
     unsigned char* dst = vbuf + (t & 1) * Lay::kTile;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) buf_load16_lds(rv, dst + (wave * LPW + i) * 1024, voff[i]);
@@ -497,18 +542,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   }
   wait_lgkmcnt0();
-  uint16_t* otile = o + (((int64_t)b * Hq + h) * (int64_t)Nq + qw0) * D;
+  uint16_t* otile = VARLEN ? o + ((q_row0 + qw0) * Hq + h) * D
+                           : o + (((int64_t)b * Hq + h) * (int64_t)Nq + qw0) * D;
   const int cl = lane % CPR, rl = lane / CPR;
 #pragma unroll
   for (int s0 = 0; s0 < 32; s0 += RPS) {
     const int r = s0 + rl;
     const u32x4_t val = *reinterpret_cast<const u32x4_t*>(qslot + r * ROW + ((cl ^ (r & (CPR - 1))) << 4));
     if (qw0 + r < Nq)
-      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(otile + (int64_t)r * D + cl * 8));
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(otile + (int64_t)r * QS + cl * 8));
   }
   if (my_row < Nq && half == 0) {
     const float out = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
-    lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
+    if constexpr (VARLEN)
+      lse[(int64_t)h * vl.total_q + q_row0 + my_row] = out;
+    else
+      lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
   }
 }
 
@@ -516,9 +565,18 @@ template <int DT, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + kFwdBM - 1) / kFwdBM;
   const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-  hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL>), dim3((unsigned)blocks), dim3(kFwdThreads),
-                     0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                     (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
+  const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
+  if (a.cu_q) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, true>), dim3((unsigned)blocks),
+                       dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale, vl);
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, false>), dim3((unsigned)blocks),
+                       dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale, vl);
+  }
   return hipGetLastError();
 }
 

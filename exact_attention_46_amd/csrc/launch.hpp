@@ -16,6 +16,11 @@ struct FwdArgs {
   float scale;
   int causal;
   int dtype;
+  // Packed variable-length batch (cu_q != nullptr): q/o [total_q, Hq, d],
+  // k/v [total_k, Hkv, d], lse [Hq, total_q]; Nq / Nk are the largest lengths.
+  const int* cu_q = nullptr;
+  const int* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 struct SplitArgs {

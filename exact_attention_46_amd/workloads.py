@@ -21,7 +21,10 @@ Recipe (all draws from ``torch.Generator`` seeded with the workload's seed):
     ``page_size`` rows ([num_pages, page_size, Hkv, d]) at the positions of a
     seeded ``randperm`` of the pool, plus ``spare`` unused pages; every row no
     sequence uses (unused pages, the tail of each sequence's last page) is NaN,
-    and unused block-table slots hold -1.
+    and unused block-table slots hold -1;
+  * packed variable-length prefill: per-sequence query and key lengths given, q
+    [total_q, Hq, d], k, v [total_k, Hkv, d] drawn in that order as fp32 ``randn``
+    and cast; cu_seqlens are the running sums of the lengths.
 """
 from __future__ import annotations
 
@@ -185,3 +188,30 @@ def paged_from_padded(k_cache, v_cache, seq_lens, page_size, seed=0, spare=3):
             kp[pg, : r1 - r0] = k_cache[b, :, r0:r1].transpose(0, 1)
             vp[pg, : r1 - r0] = v_cache[b, :, r0:r1].transpose(0, 1)
     return kp, vp, table
+
+
+def varlen_inputs(q_lens, k_lens, Hq, Hkv, d, dtype="bf16", seed=0):
+    """Returns CPU tensors (q [total_q,Hq,d], k, v [total_k,Hkv,d], cu_q, cu_k [B+1] int32)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    cu_q = torch.zeros(len(q_lens) + 1, dtype=torch.int32)
+    cu_k = torch.zeros(len(k_lens) + 1, dtype=torch.int32)
+    cu_q[1:] = torch.cumsum(torch.as_tensor(q_lens, dtype=torch.int64), 0).to(torch.int32)
+    cu_k[1:] = torch.cumsum(torch.as_tensor(k_lens, dtype=torch.int64), 0).to(torch.int32)
+    t = DTYPES[dtype]
+    q = torch.randn((int(cu_q[-1]), Hq, d), generator=g, dtype=torch.float32).to(t)
+    k = torch.randn((int(cu_k[-1]), Hkv, d), generator=g, dtype=torch.float32).to(t)
+    v = torch.randn((int(cu_k[-1]), Hkv, d), generator=g, dtype=torch.float32).to(t)
+    return q, k, v, cu_q, cu_k
+
+
+def varlen_lengths(total, n_min, n_max, seed):
+    """Seeded sequence lengths, uniform on [n_min, n_max], until they fill `total`
+    tokens (the last one is cut to fit)."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    lens = []
+    left = total
+    while left > 0:
+        n = int(torch.randint(n_min, n_max + 1, (1,), generator=g))
+        lens.append(min(n, left))
+        left -= lens[-1]
+    return lens

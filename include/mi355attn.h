@@ -72,6 +72,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_fwd_varlen — attn_fwd over a packed batch of sequences of different
+ * lengths (the variable-length mode that the flash-attention page's kernel
+ * traits carry as a flag): no padding, each sequence attends only to its own
+ * keys, with its own causal alignment.
+ *
+ *   q            [total_q, Hq,  d]   dtype  (read)
+ *   k            [total_k, Hkv, d]   dtype  (read)
+ *   v            [total_k, Hkv, d]   dtype  (read)
+ *   o            [total_q, Hq,  d]   dtype  (written, rounded to nearest even)
+ *   lse          [Hq, total_q]       float  (written)
+ *   cu_seqlens_q [B + 1]             int32, device memory (read)
+ *   cu_seqlens_k [B + 1]             int32, device memory (read)
+ *
+ * Sequence b owns query rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]); both arrays must start at 0, never
+ * decrease and end at total_q / total_k (values are clamped into [0, total]
+ * and a decrease counts as an empty sequence, so the kernel never reads or
+ * writes outside the tensors). With Nq_b and Nk_b its lengths, causal = 1
+ * allows key j for query row i iff j <= i + (Nk_b - Nq_b) (bottom-right, as in
+ * attn_fwd); a row with no allowed key gets O = 0 and LSE = -inf. max_seqlen_q
+ * sizes the grid and must be >= every Nq_b: rows of a longer sequence past
+ * max_seqlen_q are not written. Head mapping, d, dtype and scale as attn_fwd.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq, int Hkv,
+                    int total_q, int total_k, int max_seqlen_q, int d, float scale, int causal,
+                    int dtype, void* stream);
+
+/*
  * attn_decode_split — first half of split-KV ("flash decoding") decode: one new
  * query token per sequence against a padded KV cache, split into chunks of
  * `chunk` keys; each chunk emits its own normalised partial output and LSE

@@ -50,13 +50,14 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, i64, p, p, i]
         lib.oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, f, p, p, i]
+        lib.oracle_attn_fwd_varlen.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_decode_paged.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_decode_chunks.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_combine.argtypes = [p, p, p, i, i, i, i, i, p, p]
         lib.oracle_decode_values.argtypes = [p, i64, i, p]
         lib.oracle_max_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_decode,
-                   lib.oracle_decode_paged,
+                   lib.oracle_decode_paged, lib.oracle_attn_fwd_varlen,
                    lib.oracle_decode_chunks, lib.oracle_combine, lib.oracle_decode_values,
                    lib.oracle_max_threads):
             fn.restype = ctypes.c_int
@@ -120,6 +121,27 @@ def attn_fwd_rows(q, k, v, dtype: int, scale: float, causal: bool, rows, nthread
                                       float(scale), int(bool(causal)), _ptr(rows), n, _ptr(o),
                                       _ptr(lse), nthreads)
     _check(rc, "attn_fwd_rows")
+    return o, lse
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, dtype: int, scale: float, causal: bool,
+                    nthreads: int = 0):
+    """Exact attention over a packed batch: q [total_q,Hq,d], k/v [total_k,Hkv,d], cu_seqlens
+    [B+1] -> (o [total_q,Hq,d], lse [Hq,total_q])."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    cq = np.ascontiguousarray(cu_seqlens_q, dtype=np.int32)
+    ck = np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if v.shape != k.shape or dk != d or cq.shape != ck.shape or cq.ndim != 1:
+        raise ValueError("shape mismatch")
+    o = np.empty((total_q, Hq, d), dtype=np.float64)
+    lse = np.empty((Hq, total_q), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cq), _ptr(ck), dtype,
+                                        cq.shape[0] - 1, Hq, Hkv, total_q, total_k, d,
+                                        float(scale), int(bool(causal)), _ptr(o), _ptr(lse),
+                                        nthreads)
+    _check(rc, "attn_fwd_varlen")
     return o, lse
 
 

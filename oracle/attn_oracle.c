@@ -224,6 +224,71 @@ int oracle_attn_fwd_rows(const uint16_t* q, const uint16_t* k, const uint16_t* v
     return 0;
 }
 
+/*
+ * Attention forward over a packed batch of sequences of different lengths (the
+ * variable-length mode flagged in the flash-attention page's kernel traits).
+ *   q [total_q, Hq, d], k and v [total_k, Hkv, d] (16-bit patterns, row-major)
+ *   cu_q, cu_k [B+1]: sequence b owns query rows [cu_q[b], cu_q[b+1]) and key
+ *   rows [cu_k[b], cu_k[b+1]); both start at 0, never decrease and end at
+ *   total_q / total_k.
+ *   o [total_q, Hq, d] fp64, lse [Hq, total_q] fp64
+ * Each sequence is an independent attention problem with Nq_b = cu_q[b+1] -
+ * cu_q[b] queries and Nk_b keys; the causal mask is bottom-right aligned within
+ * it. Each (b, h) gathers its kv-head's key and value rows into contiguous
+ * scratch, then every query row attends to them as in oracle_attn_fwd.
+ */
+int oracle_attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                           const int32_t* cu_q, const int32_t* cu_k, int dtype, int B, int Hq,
+                           int Hkv, int total_q, int total_k, int d, float scale, int causal,
+                           double* o, double* lse, int nthreads) {
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || total_q <= 0 || total_k < 0 || d <= 0) return -1;
+    if (Hq % Hkv != 0 || (dtype != 0 && dtype != 1)) return -1;
+    if (cu_q[0] != 0 || cu_k[0] != 0 || cu_q[B] != total_q || cu_k[B] != total_k) return -1;
+    int64_t max_nk = 0;
+    for (int b = 0; b < B; ++b) {
+        if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
+        if (cu_k[b + 1] - cu_k[b] > max_nk) max_nk = cu_k[b + 1] - cu_k[b];
+    }
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t units = (int64_t)B * Hq;
+    const size_t nk_alloc = (size_t)(max_nk > 0 ? max_nk : 1);
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * nk_alloc);
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* vrow = (double*)malloc(sizeof(double) * (size_t)d);
+        uint16_t* kg = (uint16_t*)malloc(sizeof(uint16_t) * nk_alloc * (size_t)d);
+        uint16_t* vg = (uint16_t*)malloc(sizeof(uint16_t) * nk_alloc * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            const int64_t b = u / Hq, h = u % Hq;
+            const int64_t g = h * Hkv / Hq;
+            const int64_t q0 = cu_q[b], k0 = cu_k[b];
+            const int Nq = cu_q[b + 1] - cu_q[b], Nk = cu_k[b + 1] - cu_k[b];
+            /* 1. this sequence's rows of kv-head g, contiguous */
+            for (int64_t j = 0; j < Nk; ++j) {
+                const int64_t src = ((k0 + j) * Hkv + g) * (int64_t)d;
+                memcpy(kg + j * d, k + src, sizeof(uint16_t) * (size_t)d);
+                memcpy(vg + j * d, v + src, sizeof(uint16_t) * (size_t)d);
+            }
+            /* 2. every query row of the sequence */
+            for (int64_t i = 0; i < Nq; ++i) {
+                const int64_t row = q0 + i;
+                decode_vec(q + (row * Hq + h) * (int64_t)d, d, dtype, qrow);
+                attend_row(qrow, kg, vg, dtype, 0, causal_end(i, Nq, Nk, causal), d, sc, s, vrow,
+                           o + (row * Hq + h) * (int64_t)d, lse + h * (int64_t)total_q + row);
+            }
+        }
+        free(s);
+        free(qrow);
+        free(vrow);
+        free(kg);
+        free(vg);
+    }
+    return 0;
+}
+
 static int check_decode(int B, int Hq, int Hkv, int max_len, int d, int dtype,
                         const int32_t* seq_lens) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0) return -1;

@@ -84,6 +84,24 @@ def test_attn_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
 
 
+def fwd_varlen(lib, q=A, k=A, v=A, o=A2, lse=A2, cq=A, ck=A2, B=3, Hq=4, Hkv=2, total_q=100,
+               total_k=120, max_q=60, d=128, scale=0.1, causal=1, dtype=0):
+    return lib.attn_fwd_varlen(q, k, v, o, lse, cq, ck, B, Hq, Hkv, total_q, total_k, max_q, d,
+                               scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(cq=None), -1), (dict(ck=None), -1),
+    (dict(B=0), -2), (dict(total_q=0), -2), (dict(total_k=0), -2), (dict(max_q=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(max_q=2**23 + 1), -2), (dict(B=2**20, Hq=2**8, max_q=2**16), -2),
+    (dict(d=96), -3), (dict(dtype=9), -3),
+    (dict(scale=-2.0), -5), (dict(causal=3), -5),
+    (dict(v=MIS), -4), (dict(cq=ctypes.c_void_p(4098)), -4),
+])
+def test_attn_fwd_varlen_rejects(lib, kw, code):
+    assert fwd_varlen(lib, **kw) == code
+
+
 def split(lib, q=A, kc=A, vc=A, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2, max_len=64, d=128,
           chunk=16, scale=0.1, dtype=0):
     return lib.attn_decode_split(q, kc, vc, sl, po, pl, B, Hq, Hkv, max_len, d, chunk, scale,

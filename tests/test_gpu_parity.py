@@ -360,3 +360,54 @@ def test_paged_decode_full_size_matches_contiguous_and_oracle():
                                wl.bits(vc[b:b + 1, :, :L].cpu()), np.array([L], dtype=np.int32),
                                0, w.scale)
         check(o_p[b:b + 1], lse_p[b:b + 1], ro, rl, "bf16", "paged decode seq %d (L=%d)" % (b, L))
+
+
+# --------------------------------------------------------------- packed variable-length prefill
+
+VARLEN = [
+    # q_lens, k_lens, Hq, Hkv, d, dtype, causal
+    ([1, 255, 256, 257, 0, 600], [1, 255, 256, 257, 0, 600], 4, 2, 128, "bf16", True),
+    ([300, 5, 1000], [500, 5, 1000], 8, 8, 64, "fp16", True),
+    ([700, 64, 3], [100, 0, 3], 4, 1, 128, "bf16", True),
+    ([129, 513, 2], [129, 513, 2], 6, 3, 128, "bf16", False),
+    ([2048, 1536, 100], [2048, 1536, 100], 32, 8, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("q_lens,k_lens,Hq,Hkv,d,dtype,causal", VARLEN)
+def test_fwd_varlen(q_lens, k_lens, Hq, Hkv, d, dtype, causal):
+    seed = zlib.crc32(repr((q_lens, k_lens, Hq, d)).encode()) % 10000
+    q, k, v, cq, ck = wl.varlen_inputs(q_lens, k_lens, Hq, Hkv, d, dtype, seed)
+    scale = 1.0 / math.sqrt(d)
+    total_q = q.shape[0]
+    ob, o = _guarded(q.shape, q.dtype)
+    lb, lse = _guarded((Hq, total_q), torch.float32)
+    qd, kd, vd, cqd, ckd = _dev(q, k, v, cq, ck)
+    ea.attn_fwd_varlen(qd, kd, vd, o, lse, cqd, ckd, max(q_lens), causal, scale)
+    torch.cuda.synchronize()
+    assert _guard_ok(ob, o.numel()) and _guard_ok(lb, lse.numel()), "write outside the outputs"
+    ro, rl = oracle.attn_fwd_varlen(wl.bits(q), wl.bits(k), wl.bits(v), cq.numpy(), ck.numpy(),
+                                    wl.DTYPE_CODE[dtype], scale, causal)
+    check(o, lse, ro, rl, dtype, "varlen %s" % ((q_lens, k_lens, Hq, Hkv, d, dtype, causal),))
+
+
+def test_fwd_varlen_full_size_sampled():
+    """The bench's packed batch (8192 tokens, lengths U[256, 4096], Hq = Hkv = 32,
+    d = 128, causal), sampled rows of every sequence against the oracle."""
+    lens = wl.varlen_lengths(8192, 256, 4096, seed=1)
+    q, k, v, cq, ck = wl.varlen_inputs(lens, lens, 32, 32, 128, "bf16", seed=1)
+    scale = 1.0 / math.sqrt(128)
+    o, lse = ea.fwd_varlen(*_dev(q, k, v, cq, ck), max(lens), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    o, lse = o.cpu(), lse.cpu()
+    for b, n in enumerate(lens):
+        s0 = int(cq[b])
+        qb = q[s0:s0 + n].transpose(0, 1)[None].contiguous()
+        kb = k[s0:s0 + n].transpose(0, 1)[None].contiguous()
+        vb = v[s0:s0 + n].transpose(0, 1)[None].contiguous()
+        rows = _sample_rows(1, 32, n, 3, 77 + b)
+        ro, rl = oracle.attn_fwd_rows(wl.bits(qb), wl.bits(kb), wl.bits(vb), 0, scale, True, rows)
+        og = o[s0 + rows[:, 2], rows[:, 1]]
+        lg = lse[rows[:, 1], s0 + rows[:, 2]]
+        check(og, lg, ro, rl, "bf16", "varlen full size, sequence %d (N=%d)" % (b, n))

@@ -412,6 +412,60 @@ def test_paged_decode_rejects_out_of_range_pages_and_ignores_unused_slots():
         oracle.decode_paged(_bits(q), _bits(kp), _bits(vp), t, sl.numpy(), 0, 0.125)
 
 
+VARLEN_CASES = [
+    # q_lens, k_lens, Hq, Hkv, causal
+    ([5, 0, 17, 1, 33], [5, 0, 17, 1, 33], 4, 2, True),
+    ([3, 20, 7], [10, 20, 30], 4, 4, True),      # Nq < Nk: bottom-right alignment
+    ([9, 4], [2, 0], 2, 1, True),               # Nq > Nk, and a sequence with no keys
+    ([12, 30, 1], [40, 5, 9], 6, 3, False),
+]
+
+
+@pytest.mark.parametrize("q_lens,k_lens,Hq,Hkv,causal", VARLEN_CASES)
+def test_varlen_equals_each_sequence_alone(q_lens, k_lens, Hq, Hkv, causal):
+    """A packed batch is B independent problems: every sequence's rows equal the
+    dense oracle (itself pinned to SDPA and brute force) run on that sequence
+    alone, and rows with no allowed key are O = 0, LSE = -inf."""
+    q, k, v, cq, ck = wl.varlen_inputs(q_lens, k_lens, Hq, Hkv, 32, "bf16", 13)
+    o, lse = oracle.attn_fwd_varlen(_bits(q), _bits(k), _bits(v), cq.numpy(), ck.numpy(), 0,
+                                    0.2, causal)
+    for b in range(len(q_lens)):
+        qs, qe, ks, ke = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        if qe == qs:
+            continue
+        if ke == ks:
+            assert (o[qs:qe] == 0).all() and np.isneginf(lse[:, qs:qe]).all()
+            continue
+        qb = q[qs:qe].transpose(0, 1)[None].contiguous()
+        kb = k[ks:ke].transpose(0, 1)[None].contiguous()
+        vb = v[ks:ke].transpose(0, 1)[None].contiguous()
+        ro, rl = oracle.attn_fwd(_bits(qb), _bits(kb), _bits(vb), 0, 0.2, causal)
+        assert np.array_equal(o[qs:qe], ro[0].transpose(1, 0, 2))
+        assert np.array_equal(lse[:, qs:qe], rl[0])
+
+
+def test_varlen_matches_brute_force_with_uneven_lengths():
+    q_lens, k_lens = [7, 3], [11, 3]
+    q, k, v, cq, ck = wl.varlen_inputs(q_lens, k_lens, 2, 2, 16, "fp16", 4)
+    o, lse = oracle.attn_fwd_varlen(_bits(q), _bits(k), _bits(v), cq.numpy(), ck.numpy(), 1,
+                                    0.25, True)
+    for b in range(2):
+        qs, qe, ks, ke = int(cq[b]), int(cq[b + 1]), int(ck[b]), int(ck[b + 1])
+        bo, bl = brute_force(_f64(q[qs:qe].transpose(0, 1)[None]),
+                             _f64(k[ks:ke].transpose(0, 1)[None]),
+                             _f64(v[ks:ke].transpose(0, 1)[None]), 0.25, True)
+        assert np.abs(o[qs:qe] - bo[0].transpose(1, 0, 2)).max() < 1e-12
+        assert np.abs(lse[:, qs:qe] - bl[0]).max() < 1e-12
+
+
+def test_varlen_rejects_inconsistent_offsets():
+    q, k, v, cq, ck = wl.varlen_inputs([4, 4], [4, 4], 2, 2, 16, "bf16", 1)
+    bad = cq.numpy().copy()
+    bad[1] = 9  # decreasing
+    with pytest.raises(ValueError):
+        oracle.attn_fwd_varlen(_bits(q), _bits(k), _bits(v), bad, ck.numpy(), 0, 0.25, True)
+
+
 def test_oracle_rejects_bad_arguments():
     q = np.zeros((1, 3, 4, 8), dtype=np.uint16)
     k = np.zeros((1, 2, 4, 8), dtype=np.uint16)
