@@ -98,11 +98,19 @@ __device__ __forceinline__ int v_swz(int row) {
 // in its L2.
 constexpr int kFwdL2Units = 8;
 
+// Packed variable-length batches (spread = true) take the plain order instead:
+// consecutive workgroups, which land on consecutive XCDs, take consecutive
+// units, so every XCD gets the same share of every sequence (a contiguous block
+// of units per XCD would hand whole long sequences to a few XCDs); all query
+// tiles of a unit still land on one XCD when the unit count is a multiple of 8.
 __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group, int causal,
-                                            int& unit, int& qtile) {
+                                            bool spread, int& unit, int& qtile) {
   constexpr int G = kFwdL2Units;
   int rank;
-  if (units % 8 == 0 && (units / 8) % G == 0 && G % group == 0) {
+  if (spread) {
+    rank = L / units;
+    unit = L % units;
+  } else if (units % 8 == 0 && (units / 8) % G == 0 && G % group == 0) {
     const int upx = units / 8;
     const int x = L % 8, s = L / 8;
     const int grp = s / (G * nqt), r = s % (G * nqt);
@@ -156,7 +164,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nqt = (Nq + kFwdBM - 1) / kFwdBM;
   const int group = Hq / Hkv;
   int unit, qtile;
-  fwd_tile_of(blockIdx.x, B * Hq, nqt, group, CAUSAL ? 1 : 0, unit, qtile);
+  fwd_tile_of(blockIdx.x, B * Hq, nqt, group, CAUSAL ? 1 : 0, VARLEN, unit, qtile);
   const int b = unit / Hq;
   const int h = unit % Hq;
   const int g = h / group;  // == floor(h * Hkv / Hq) since Hq % Hkv == 0
