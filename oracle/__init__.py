@@ -50,6 +50,7 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, i64, p, p, i]
         lib.oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, f, p, p, i]
+        lib.oracle_attn_bwd.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, p, i]
         lib.oracle_attn_fwd_varlen.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_decode_paged.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_decode_chunks.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, p, p, i]
@@ -57,7 +58,7 @@ def _load():
         lib.oracle_decode_values.argtypes = [p, i64, i, p]
         lib.oracle_max_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_decode,
-                   lib.oracle_decode_paged, lib.oracle_attn_fwd_varlen,
+                   lib.oracle_decode_paged, lib.oracle_attn_fwd_varlen, lib.oracle_attn_bwd,
                    lib.oracle_decode_chunks, lib.oracle_combine, lib.oracle_decode_values,
                    lib.oracle_max_threads):
             fn.restype = ctypes.c_int
@@ -122,6 +123,24 @@ def attn_fwd_rows(q, k, v, dtype: int, scale: float, causal: bool, rows, nthread
                                       _ptr(lse), nthreads)
     _check(rc, "attn_fwd_rows")
     return o, lse
+
+
+def attn_bwd(q, k, v, dout, dtype: int, scale: float, causal: bool, nthreads: int = 0):
+    """Gradients of sum(dout * O) for O = attention(q, k, v): q/dout [B,Hq,Nq,d], k/v
+    [B,Hkv,Nk,d] -> (dq, dk, dv) fp64 of the same shapes."""
+    q, k, v, do = _u16(q), _u16(k), _u16(v), _u16(dout)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk_ = k.shape
+    if v.shape != k.shape or do.shape != q.shape or Bk != B or dk_ != d:
+        raise ValueError("shape mismatch")
+    dq = np.empty(q.shape, dtype=np.float64)
+    dk = np.empty(k.shape, dtype=np.float64)
+    dv = np.empty(k.shape, dtype=np.float64)
+    rc = _load().oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(do), dtype, B, Hq, Hkv, Nq, Nk,
+                                 d, float(scale), int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 nthreads)
+    _check(rc, "attn_bwd")
+    return dq, dk, dv
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, dtype: int, scale: float, causal: bool,

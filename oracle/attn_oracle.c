@@ -289,6 +289,102 @@ int oracle_attn_fwd_varlen(const uint16_t* q, const uint16_t* k, const uint16_t*
     return 0;
 }
 
+/*
+ * Attention backward: the gradients of L = sum_i dO_i . O_i with respect to q, k
+ * and v, written out from the plain definition (the derivation that the
+ * llm.c page's attention_backward and the flash-attention page's backward
+ * kernel implement): for each query row i with allowed keys J_i,
+ *   P_ij  = exp(s_ij) / sum_{j' in J_i} exp(s_ij')     s_ij = scale * q_i . k_j
+ *   dv_j += P_ij dO_i
+ *   dP_ij = dO_i . v_j
+ *   D_i   = sum_j P_ij dP_ij
+ *   dS_ij = P_ij (dP_ij - D_i)
+ *   dq_i  = scale * sum_j dS_ij k_j,     dk_j += scale * dS_ij q_i
+ * dk and dv of kv-head g sum over every query head that reads it (GQA).
+ *   q, do [B,Hq,Nq,d]; k, v [B,Hkv,Nk,d] (16-bit patterns)
+ *   dq [B,Hq,Nq,d], dk, dv [B,Hkv,Nk,d] fp64
+ * Parallel over (b, kv-head), so each thread owns its dk / dv rows.
+ */
+int oracle_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                    const uint16_t* dout, int dtype, int B, int Hq, int Hkv, int Nq, int Nk,
+                    int d, float scale, int causal, double* dq, double* dk, double* dv,
+                    int nthreads) {
+    if (check_fwd(B, Hq, Hkv, Nq, Nk, d, dtype)) return -1;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t units = (int64_t)B * Hkv;
+    const int group = Hq / Hkv;
+#pragma omp parallel
+    {
+        double* sp = (double*)malloc(sizeof(double) * (size_t)Nk);   /* scores, then P */
+        double* dp = (double*)malloc(sizeof(double) * (size_t)Nk);   /* dP, then dS */
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* dorow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* kd = (double*)malloc(sizeof(double) * (size_t)Nk * (size_t)d);
+        double* vd = (double*)malloc(sizeof(double) * (size_t)Nk * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            const int64_t b = u / Hkv, g = u % Hkv;
+            const int64_t kvbase = ((b * Hkv + g) * (int64_t)Nk) * d;
+            decode_vec(k + kvbase, (int64_t)Nk * d, dtype, kd);
+            decode_vec(v + kvbase, (int64_t)Nk * d, dtype, vd);
+            double* dkh = dk + kvbase;
+            double* dvh = dv + kvbase;
+            for (int64_t x = 0; x < (int64_t)Nk * d; ++x) dkh[x] = dvh[x] = 0.0;
+            for (int hh = 0; hh < group; ++hh) {
+                const int64_t h = g * group + hh;  /* the heads with floor(h*Hkv/Hq) == g */
+                for (int64_t i = 0; i < Nq; ++i) {
+                    const int64_t qoff = ((b * Hq + h) * (int64_t)Nq + i) * d;
+                    double* dqi = dq + qoff;
+                    for (int t = 0; t < d; ++t) dqi[t] = 0.0;
+                    const int64_t hi = causal_end(i, Nq, Nk, causal);
+                    if (hi <= 0) continue;  /* no allowed key: no gradient */
+                    decode_vec(q + qoff, d, dtype, qrow);
+                    decode_vec(dout + qoff, d, dtype, dorow);
+                    /* P_i: scores, max, exponentials, normalisation */
+                    double m = -INFINITY;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        double acc = 0.0;
+                        for (int t = 0; t < d; ++t) acc += qrow[t] * kd[j * d + t];
+                        sp[j] = sc * acc;
+                        if (sp[j] > m) m = sp[j];
+                    }
+                    double l = 0.0;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        sp[j] = exp(sp[j] - m);
+                        l += sp[j];
+                    }
+                    for (int64_t j = 0; j < hi; ++j) sp[j] /= l;
+                    /* dP_ij and D_i */
+                    double Di = 0.0;
+                    for (int64_t j = 0; j < hi; ++j) {
+                        double acc = 0.0;
+                        for (int t = 0; t < d; ++t) acc += dorow[t] * vd[j * d + t];
+                        dp[j] = acc;
+                        Di += sp[j] * acc;
+                    }
+                    /* dS, then the three gradients */
+                    for (int64_t j = 0; j < hi; ++j) {
+                        const double ds = sp[j] * (dp[j] - Di);
+                        for (int t = 0; t < d; ++t) {
+                            dqi[t] += sc * ds * kd[j * d + t];
+                            dkh[j * d + t] += sc * ds * qrow[t];
+                            dvh[j * d + t] += sp[j] * dorow[t];
+                        }
+                    }
+                }
+            }
+        }
+        free(sp);
+        free(dp);
+        free(qrow);
+        free(dorow);
+        free(kd);
+        free(vd);
+    }
+    return 0;
+}
+
 static int check_decode(int B, int Hq, int Hkv, int max_len, int d, int dtype,
                         const int32_t* seq_lens) {
     if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0) return -1;

@@ -466,6 +466,102 @@ def test_varlen_rejects_inconsistent_offsets():
         oracle.attn_fwd_varlen(_bits(q), _bits(k), _bits(v), bad, ck.numpy(), 0, 0.25, True)
 
 
+def _torch_grads(q, k, v, do, scale, causal):
+    """fp64 autograd through torch's scaled_dot_product_attention (library
+    routine) with an explicit bottom-right causal mask; GQA by repeating K/V,
+    whose autograd sums the group's gradients."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    qt, kt, vt = (t.double().requires_grad_(True) for t in (q, k, v))
+    kr = kt.repeat_interleave(Hq // Hkv, dim=1)
+    vr = vt.repeat_interleave(Hq // Hkv, dim=1)
+    mask = None
+    if causal:
+        i = torch.arange(Nq)[:, None]
+        j = torch.arange(Nk)[None, :]
+        mask = j <= i + (Nk - Nq)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kr, vr, attn_mask=mask, scale=scale)
+    (o * do.double()).sum().backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+BWD_CASES = [
+    # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 2, 2, 9, 9, 16, True),
+    (2, 4, 2, 13, 13, 32, False),
+    (1, 4, 1, 6, 15, 16, True),    # Nq < Nk, bottom-right
+    (1, 2, 2, 17, 17, 64, True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,causal", BWD_CASES)
+def test_backward_matches_torch_autograd_fp64(B, Hq, Hkv, Nq, Nk, d, causal):
+    q = _rand((B, Hq, Nq, d), "bf16", 31)
+    k = _rand((B, Hkv, Nk, d), "bf16", 32)
+    v = _rand((B, Hkv, Nk, d), "bf16", 33)
+    do = _rand((B, Hq, Nq, d), "bf16", 34)
+    scale = float(np.float32(1.0 / math.sqrt(d)))  # the fp32 value the oracle receives
+    dq, dk, dv = oracle.attn_bwd(_bits(q), _bits(k), _bits(v), _bits(do), 0, scale, causal)
+    tq, tk, tv = _torch_grads(q, k, v, do, scale, causal)
+    assert np.abs(dq - tq).max() < 1e-11
+    assert np.abs(dk - tk).max() < 1e-11
+    assert np.abs(dv - tv).max() < 1e-11
+
+
+def test_backward_matches_finite_differences_of_the_forward():
+    """Central differences of L = sum(dO * O), O from the forward oracle, with
+    each probed input moved by one fp16 ulp either way (exact in the 16-bit
+    inputs); truncation error is O(ulp^2)."""
+    B, H, N, d = 1, 2, 7, 8
+    q = _rand((B, H, N, d), "fp16", 41)
+    k = _rand((B, H, N, d), "fp16", 42)
+    v = _rand((B, H, N, d), "fp16", 43)
+    do = _rand((B, H, N, d), "fp16", 44)
+    scale = 0.3
+    dq, dk, dv = oracle.attn_bwd(_bits(q), _bits(k), _bits(v), _bits(do), 1, scale, True)
+    dof = _f64(do)
+
+    def loss(qq, kk, vv):
+        o, _ = oracle.attn_fwd(_bits(qq), _bits(kk), _bits(vv), 1, scale, True)
+        return float((o * dof).sum())
+
+    rng = np.random.default_rng(3)
+    for which, grad in (("q", dq), ("k", dk), ("v", dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in (B, H, N, d))
+            t = {"q": q, "k": k, "v": v}[which]
+            bits = t.view(torch.int16).clone()
+            up, dn = t.clone(), t.clone()
+            up.view(torch.int16)[idx] = bits[idx] + (1 if float(t[idx]) >= 0 else -1)
+            dn.view(torch.int16)[idx] = bits[idx] - (1 if float(t[idx]) >= 0 else -1)
+            h = float(up[idx]) - float(dn[idx])
+            args_up = {"q": q, "k": k, "v": v}
+            args_dn = dict(args_up)
+            args_up[which], args_dn[which] = up, dn
+            fd = (loss(**{a + a: b for a, b in args_up.items()})
+                  - loss(**{a + a: b for a, b in args_dn.items()})) / h
+            assert abs(fd - grad[idx]) < 1e-5 * max(1.0, abs(grad[idx])), (which, idx, fd,
+                                                                            grad[idx])
+
+
+def test_backward_closed_form_sums():
+    """Sum over keys of dv_j equals the sum of dO over the rows that see any key
+    (the rows of P sum to one); sum over keys of dk_j is zero (each row of dS
+    sums to zero). Both per (b, kv-head), over the group's query heads."""
+    B, Hq, Hkv, N, d = 2, 4, 2, 11, 16
+    q = _rand((B, Hq, N, d), "bf16", 51)
+    k = _rand((B, Hkv, N, d), "bf16", 52)
+    v = _rand((B, Hkv, N, d), "bf16", 53)
+    do = _rand((B, Hq, N, d), "bf16", 54)
+    dq, dk, dv = oracle.attn_bwd(_bits(q), _bits(k), _bits(v), _bits(do), 0, 0.25, True)
+    dof = _f64(do)
+    for b in range(B):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if h * Hkv // Hq == g]
+            assert np.abs(dv[b, g].sum(axis=0) - dof[b, heads].sum(axis=(0, 1))).max() < 1e-12
+            assert np.abs(dk[b, g].sum(axis=0)).max() < 1e-12
+
+
 def test_oracle_rejects_bad_arguments():
     q = np.zeros((1, 3, 4, 8), dtype=np.uint16)
     k = np.zeros((1, 2, 4, 8), dtype=np.uint16)
