@@ -10,6 +10,8 @@ every timed step.
 Prints ONE JSON line:
   value       prefill TFLOP/s = 4*B*H*N*N*d/2 / mean forward kernel time
   decode      KV GB/s = sum_b 2*Hkv*L_b*d*2 bytes / mean (split + combine) time
+  bwd           the backward (dQ, dK, dV) on the prefill workload, TFLOP/s at 2.5x
+                the forward's flops, timed in a loop of its own
   fwd_varlen    a packed causal prefill batch (8192 tokens in sequences of seeded
                 lengths U[256, 4096]), TFLOP/s, timed in a loop of its own
   decode_paged  the same decode over a paged cache (64-row pages, shuffled pool,
@@ -48,6 +50,8 @@ def parse():
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-bwd", action="store_true",
+                    help="skip the backward measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement")
     ap.add_argument("--no-paged", action="store_true",
@@ -186,6 +190,40 @@ def cpu_baseline(w, q, k, v, target_s):
 
 PAGE_SIZE = 64
 VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX = 8192, 256, 4096
+
+
+def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
+    """Backward on the llm_prefill workload (dO drawn like the inputs). TFLOP/s with
+    the usual convention: 2.5x the forward's flops (five products of the forward's
+    size); the kernels perform seven (S and dP are recomputed by both the dK/dV
+    and the dQ kernels). Timed in a loop of its own after the steps."""
+    print("bench: backward", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(wp.seed + 100)
+    do = torch.randn(qg.shape, generator=g).to(qg.dtype).to(qg.device)
+    dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
+    delta = torch.empty_like(lseg)
+
+    def run():
+        ea.attn_bwd(qg, kg, vg, og, do, lseg, delta, dq, dk, dv, True, wp.scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    n = max(5, args.steps // 5)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    flops = 2.5 * 4.0 * wp.B * wp.Hq * wp.N * wp.N * wp.d / 2.0
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "flop_convention": "2.5 x forward (causal halved)",
+            "roofline": {"kernel": "attn_bwd (delta + dkdv + dq kernels)", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
 def bench_varlen(args, torch, np, ea, wl, dev, stream):
@@ -385,6 +423,8 @@ def main():
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                       "frac": round(gbs / PEAK_HBM_GBS, 4),
                                       "traffic": load_traffic("attn_decode_split_kernel/decode")}}
+    if do_pre and not args.no_bwd:
+        out["bwd"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream)
     if do_pre and not args.no_varlen:
         out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
     if do_dec and not args.no_paged:

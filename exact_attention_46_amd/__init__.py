@@ -8,8 +8,10 @@ no CPU fallback.
 """
 from ._binding import (  # noqa: F401
     AttnError,
+    bwd,
     EXPORTS,
     LIB_PATH,
+    attn_bwd,
     attn_decode_combine,
     attn_decode_split,
     attn_decode_split_paged,

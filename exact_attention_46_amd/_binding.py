@@ -27,8 +27,8 @@ ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_decode_split", "attn_decode_split_paged",
-           "attn_decode_combine", "attn_status_str")
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_decode_split",
+           "attn_decode_split_paged", "attn_decode_combine", "attn_status_str")
 
 _DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 
@@ -52,6 +52,7 @@ def load_library() -> ctypes.CDLL:
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
+        lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
         lib.attn_decode_split_paged.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f,
                                                 i, p]
@@ -59,6 +60,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_status_str.argtypes = [i]
         lib.attn_fwd.restype = i
         lib.attn_fwd_varlen.restype = i
+        lib.attn_bwd.restype = i
         lib.attn_decode_split.restype = i
         lib.attn_decode_split_paged.restype = i
         lib.attn_decode_combine.restype = i
@@ -116,6 +118,39 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                                  _stream(stream))
     if st != OK:
         raise AttnError("attn_fwd", st)
+
+
+def attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool, scale: float,
+             stream=None) -> None:
+    """Calls attn_bwd. q/o/dout/dq [B,Hq,Nq,d]; k/v/dk/dv [B,Hkv,Nk,d]; lse and the
+    workspace delta [B,Hq,Nq] fp32."""
+    _gpu(q, k, v, o, dout, lse, delta, dq, dk, dv)
+    _need(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D, k ~ v")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape[0] == B and k.shape[3] == d, "k/v batch or head dim differ from q")
+    for t in (k, v, o, dout, dq, dk, dv):
+        _need(t.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape and dout.shape == q.shape and dq.shape == q.shape,
+          "o, dout, dq must have q's shape")
+    _need(dk.shape == k.shape and dv.shape == k.shape, "dk, dv must have k's shape")
+    for t in (lse, delta):
+        _need(t.dtype == torch.float32 and tuple(t.shape) == (B, Hq, Nq), "lse/delta [B,Hq,Nq] fp32")
+    st = load_library().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                 _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d,
+                                 float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_bwd", st)
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, stream=None):
+    """Allocates and returns (dq, dk, dv) for attention backward."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, causal, scale, stream)
+    return dq, dk, dv
 
 
 def attn_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,

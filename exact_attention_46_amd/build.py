@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmi355attn.so")
-SOURCES = ["abi.hip", "attn_fwd.hip", "attn_decode.hip"]
+SOURCES = ["abi.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_decode.hip"]
 # Extra flags per source. The kernels never see a signalling NaN (their
 # inputs to max() come from MFMA and FMA results), so the compiler need not
 # quiet operands before each max; argument checking in abi.hip keeps full NaN

@@ -39,6 +39,26 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, float* delta, void* dq, void* dk,
+                        void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
+    return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || Nq > kMaxSeq || Nk > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(delta, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::bwd_grid_blocks(B, Hq, Hkv, Nq, Nk) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                       causal, dtype};
+  return from_hip(mi355attn::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                const int* cu_seqlens_q, const int* cu_seqlens_k, int B, int Hq,
                                int Hkv, int total_q, int total_k, int max_seqlen_q, int d,

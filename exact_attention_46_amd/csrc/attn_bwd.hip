@@ -1,0 +1,421 @@
+// Exact attention backward for gfx950: the gradients dQ, dK, dV of
+// L = sum(dO * O) for O = softmax(scale * Q K^T + causal mask) V, recomputing the
+// probabilities from the forward's per-row LSE instead of storing them (the
+// backward of the flash-attention page's kernel and the attention_backward of
+// the llm.c page compute the same quantities):
+//   D_i   = sum_t dO_it O_it
+//   P_ij  = exp(scale * q_i.k_j - LSE_i)          (0 for masked keys)
+//   dP_ij = dO_i . v_j
+//   dS_ij = P_ij (dP_ij - D_i)
+//   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
+// dK and dV of kv-head g sum over the query heads that read it (GQA).
+//
+// Three kernels on one stream, no atomics (the result is deterministic):
+//  * attn_bwd_delta_kernel: D for every query row.
+//  * attn_bwd_dkdv_kernel: one workgroup per (batch, kv-head, 128 keys); each of
+//    its 4 waves owns 32 keys, whose K and V rows it keeps in registers as the
+//    B operands of S = Q K^T and dP = dO V^T (32x32x16 MFMA, fp32 accumulate).
+//    It walks 32-row tiles of Q and dO (every query head of the group) staged in
+//    LDS. The S / dP accumulators hold one key per lane and 16 rows per lane,
+//    which is the B-operand layout of the next products, so P and dS enter
+//    dV^T += dO^T P and dK^T += Q^T dS as they are (rounded to the input dtype),
+//    with dO^T and Q^T read from the staged tiles by transposing LDS reads.
+//  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (batch, head);
+//    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
+//    of K and V staged in LDS: S^T = K Q^T, dP^T = V dO^T (one query row per
+//    lane), dS^T, then dQ^T += K^T dS^T with K^T from transposing reads.
+// The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
+// instead of 5), which is what removes the atomics on dQ.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace mi355attn {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+constexpr int kBwdKeysWG = 32 * kBwdWaves;  // keys per dK/dV workgroup
+constexpr int kBwdRowsWG = 32 * kBwdWaves;  // query rows per dQ workgroup
+constexpr int kBwdQT = 32;                  // query rows per dK/dV step
+constexpr int kBwdKT = 64;                  // keys per dQ step
+
+// LDS tiles are row-major with the 16-byte chunk index XOR-swizzled by the low
+// bits of the row (as the forward's K tile), read both as rows (16-byte reads)
+// and transposed (ds_read_b64_tr_b16).
+template <int D>
+__device__ __forceinline__ int bwd_swz(int row) {
+  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+}
+
+// Stages rows [r0, r0 + ROWS) of a [*, D] row-major tensor (rows >= n read as
+// zero) into an LDS tile: all threads of the workgroup take part, each load
+// moves 1 KiB.
+template <int D, int ROWS>
+__device__ __forceinline__ void stage_rows(const uint16_t* base, int r0, int n, unsigned char* tile,
+                                           int tid) {
+  constexpr int ROW = D * 2, CH = D / 8, RPL = 64 / CH;
+  constexpr int LOADS = ROWS / RPL;  // 1 KiB loads for the tile
+  static_assert(LOADS % kBwdWaves == 0, "loads split evenly over the waves");
+  const int wave = tid >> 6, lane = tid & 63;
+  const int rows_valid = n - r0;  // > 0 for every staged tile
+  const auto rs = make_rsrc(base + (int64_t)r0 * D, (uint32_t)rows_valid * ROW);
+#pragma unroll
+  for (int i = 0; i < LOADS / kBwdWaves; ++i) {
+    const int ld = wave * (LOADS / kBwdWaves) + i;
+    const int row = ld * RPL + lane / CH;
+    const int pc = lane % CH;
+    buf_load16_lds(rs, tile + ld * 1024, (uint32_t)row * ROW + (uint32_t)((pc ^ bwd_swz<D>(row)) << 4));
+  }
+}
+
+// A-operand row read of a staged tile: row r, logical 16-byte chunk c.
+template <int D>
+__device__ __forceinline__ u32x4_t tile_row16(const unsigned char* tile, int r, int c) {
+  return *reinterpret_cast<const u32x4_t*>(tile + r * (D * 2) + ((c ^ bwd_swz<D>(r)) << 4));
+}
+
+// Transposed A operand of step ks (16 tile rows 16ks..16ks+15) for output
+// block db (32 columns of d): lane l supplies d index 32db + l%32 and, in
+// k-slot m, tile row 16ks + 8(m/4) + 4(l/32) + m%4 -- the slot order of the
+// accumulator rows of S / dP, so P and dS serve as B operands unchanged.
+// Within each 16-lane group, source lane 4kk + a addresses row 4half + kk
+// (+8 for the second read) at columns 32db + 16((l>>4)&1) + 4a.
+template <int D>
+__device__ __forceinline__ u32x4_t tile_tr(const unsigned char* tile, int ks, int db, int lane) {
+  constexpr int ROW = D * 2;
+  const int half = lane >> 5, kk = (lane & 15) >> 2, a = lane & 3;
+  const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * a;
+  const int r1 = 16 * ks + 4 * half + kk, r2 = r1 + 8;
+  const unsigned char* p1 = tile + r1 * ROW + (((col >> 3) ^ bwd_swz<D>(r1)) << 4) + (col & 7) * 2;
+  const unsigned char* p2 = tile + r2 * ROW + (((col >> 3) ^ bwd_swz<D>(r2)) << 4) + (col & 7) * 2;
+  const u32x2_t lo = lds_read_tr16(p1), hi = lds_read_tr16(p2);
+  return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+
+template <int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                      float* __restrict__ delta, int64_t rows, int dt) {
+  // 16 lanes per row, 8 elements (16 bytes) per lane at d = 128, 4 at d = 64.
+  constexpr int PER = D / 16;
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* po = o + row * D + sub * PER;
+    const uint16_t* pd = dout + row * D + sub * PER;
+#pragma unroll
+    for (int i = 0; i < PER; i += 2) {
+      const uint32_t wo = *reinterpret_cast<const uint32_t*>(po + i);
+      const uint32_t wd = *reinterpret_cast<const uint32_t*>(pd + i);
+      float o0, o1, d0, d1;
+      if (dt == kBF16) {
+        o0 = __uint_as_float(wo << 16);
+        o1 = __uint_as_float(wo & 0xffff0000u);
+        d0 = __uint_as_float(wd << 16);
+        d1 = __uint_as_float(wd & 0xffff0000u);
+      } else {
+        const f16x2_t ho = __builtin_bit_cast(f16x2_t, wo), hd = __builtin_bit_cast(f16x2_t, wd);
+        o0 = (float)ho[0];
+        o1 = (float)ho[1];
+        d0 = (float)hd[0];
+        d1 = (float)hd[1];
+      }
+      acc = __builtin_fmaf(o0, d0, acc);
+      acc = __builtin_fmaf(o1, d1, acc);
+    }
+  }
+#pragma unroll
+  for (int sh = 8; sh >= 1; sh >>= 1) acc += __shfl_xor(acc, sh, 16);
+  if (row < rows && sub == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------- dK, dV
+
+template <int DT, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdThreads, 1)
+attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                     const float* __restrict__ lse, const float* __restrict__ delta,
+                     uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int Hq, int Hkv,
+                     int Nq, int Nk, float scale) {
+  constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
+  constexpr int TILE = kBwdQT * ROW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILE];
+  unsigned char* tq = smem;
+  unsigned char* tdo = smem + TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, half = lane >> 5;
+  const int nkt = (Nk + kBwdKeysWG - 1) / kBwdKeysWG;
+  const int kt = blockIdx.x % nkt;
+  const int unit = blockIdx.x / nkt;  // b * Hkv + g
+  const int b = unit / Hkv, g = unit % Hkv;
+  const int group = Hq / Hkv;
+  const int off = Nk - Nq;  // bottom-right causal alignment
+  const int k0 = kt * kBwdKeysWG;
+  const int kw0 = k0 + 32 * wave;     // first key of this wave
+  const int my_key = kw0 + r32;       // this lane's key (column of S / dP)
+
+  // K and V rows of the wave's keys as B operands: lane key r32, chunk
+  // half*DS + ds (keys >= Nk read as zero).
+  const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  u32x4_t kf[DS], vf[DS];
+  {
+    const int valid = max(0, min(32, Nk - kw0));
+    const auto rk = make_rsrc(k + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
+    const auto rv = make_rsrc(v + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const uint32_t o16 = (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4);
+      kf[ds] = buf_load16(rk, o16);
+      vf[ds] = buf_load16(rv, o16);
+    }
+  }
+  f32x16_t dka[DB], dva[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) {
+    dka[db] = (f32x16_t){};
+    dva[db] = (f32x16_t){};
+  }
+  const float c = scale * kLog2e;
+
+  // Query rows that may see any key of this workgroup: i >= k0 - off.
+  const int r_begin = CAUSAL ? max(0, k0 - off) : 0;
+  const int t_begin = r_begin / kBwdQT;
+  const int t_end = (Nq + kBwdQT - 1) / kBwdQT;
+  for (int hh = 0; hh < group; ++hh) {
+    const int h = g * group + hh;
+    const int64_t qoff = ((int64_t)b * Hq + h) * (int64_t)Nq;  // row index of (b, h, 0)
+    for (int t = t_begin; t < t_end; ++t) {
+      const int r0 = t * kBwdQT;
+      __syncthreads();  // the previous tile's reads are done
+      stage_rows<D, kBwdQT>(q + qoff * D, r0, Nq, tq, tid);
+      stage_rows<D, kBwdQT>(dout + qoff * D, r0, Nq, tdo, tid);
+      // This lane's rows: r0 + 8*(e/4) + 4*half + e%4 -> LSE (log2 units) and D.
+      float l2[16], dl[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int row = r0 + 8 * gq + 4 * half + x;
+          const bool ok = row < Nq;
+          l2[4 * gq + x] = ok ? lse[qoff + row] * kLog2e : 0.f;
+          dl[4 * gq + x] = ok ? delta[qoff + row] : 0.f;
+        }
+      }
+      wait_all_memory();
+      __syncthreads();
+
+      // S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys.
+      f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        s = mfma32x32x16<DT>(tile_row16<D>(tq, r32, half * DS + ds), kf[ds], s);
+        dp = mfma32x32x16<DT>(tile_row16<D>(tdo, r32, half * DS + ds), vf[ds], dp);
+      }
+      float p[16], dsv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = r0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
+        p[e] = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2[e])) : 0.f;
+        dsv[e] = p[e] * (dp[e] - dl[e]);
+      }
+      u32x4_t pf[2], sf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        pf[ks] = (u32x4_t){pack2<DT>(p[8 * ks + 0], p[8 * ks + 1]), pack2<DT>(p[8 * ks + 2], p[8 * ks + 3]),
+                           pack2<DT>(p[8 * ks + 4], p[8 * ks + 5]), pack2<DT>(p[8 * ks + 6], p[8 * ks + 7])};
+        sf[ks] = (u32x4_t){pack2<DT>(dsv[8 * ks + 0], dsv[8 * ks + 1]),
+                           pack2<DT>(dsv[8 * ks + 2], dsv[8 * ks + 3]),
+                           pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
+                           pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (d x keys).
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          dva[db] = mfma32x32x16<DT>(tile_tr<D>(tdo, ks, db, lane), pf[ks], dva[db]);
+          dka[db] = mfma32x32x16<DT>(tile_tr<D>(tq, ks, db, lane), sf[ks], dka[db]);
+        }
+    }
+  }
+
+  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane key r32, d = 32db + 8(e/4) + 4half + e%4.
+  if (my_key < Nk) {
+    uint16_t* pk = dk + kvoff + (int64_t)my_key * D;
+    uint16_t* pv = dv + kvoff + (int64_t)my_key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * half;
+        *reinterpret_cast<u32x2_t*>(pk + d0) =
+            (u32x2_t){pack2<DT>(dka[db][4 * gq + 0] * scale, dka[db][4 * gq + 1] * scale),
+                      pack2<DT>(dka[db][4 * gq + 2] * scale, dka[db][4 * gq + 3] * scale)};
+        *reinterpret_cast<u32x2_t*>(pv + d0) =
+            (u32x2_t){pack2<DT>(dva[db][4 * gq + 0], dva[db][4 * gq + 1]),
+                      pack2<DT>(dva[db][4 * gq + 2], dva[db][4 * gq + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+
+template <int DT, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdThreads, 1)
+attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                   const float* __restrict__ lse, const float* __restrict__ delta,
+                   uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
+  constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
+  constexpr int TILE = kBwdKT * ROW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILE];
+  unsigned char* tk = smem;
+  unsigned char* tv = smem + TILE;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, half = lane >> 5;
+  const int nqt = (Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  const int qt = blockIdx.x % nqt;
+  const int unit = blockIdx.x / nqt;  // b * Hq + h
+  const int b = unit / Hq, h = unit % Hq;
+  const int g = h / (Hq / Hkv);
+  const int off = Nk - Nq;
+  const int q0 = qt * kBwdRowsWG;
+  const int qw0 = q0 + 32 * wave;
+  const int my_row = qw0 + r32;  // this lane's query row (column of S^T)
+  const int64_t qrow0 = ((int64_t)b * Hq + h) * (int64_t)Nq;
+  const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+
+  // Q^T and dO^T B operands: lane row r32, chunk half*DS + ds (rows >= Nq zero).
+  u32x4_t qf[DS], dof[DS];
+  {
+    const int valid = max(0, min(32, Nq - qw0));
+    const auto rq = make_rsrc(q + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
+    const auto rd = make_rsrc(dout + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const uint32_t o16 = (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4);
+      qf[ds] = buf_load16(rq, o16);
+      dof[ds] = buf_load16(rd, o16);
+    }
+  }
+  const bool row_ok = my_row < Nq;
+  const float l2 = row_ok ? lse[qrow0 + my_row] * kLog2e : 0.f;
+  const float dl = row_ok ? delta[qrow0 + my_row] : 0.f;
+  const float c = scale * kLog2e;
+  f32x16_t dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = (f32x16_t){};
+
+  // Keys the workgroup's rows may see: [0, kv_end).
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kBwdRowsWG, Nq) - 1 + off + 1));
+  const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = t * kBwdKT;
+    __syncthreads();
+    stage_rows<D, kBwdKT>(k + kvoff, k0, Nk, tk, tid);
+    stage_rows<D, kBwdKT>(v + kvoff, k0, Nk, tv, tid);
+    wait_all_memory();
+    __syncthreads();
+
+    // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = (f32x16_t){};
+      dp[kb] = (f32x16_t){};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        s[kb] = mfma32x32x16<DT>(tile_row16<D>(tk, 32 * kb + r32, half * DS + ds), qf[ds], s[kb]);
+        dp[kb] = mfma32x32x16<DT>(tile_row16<D>(tv, 32 * kb + r32, half * DS + ds), dof[ds], dp[kb]);
+      }
+    }
+    // dS^T, packed as the B operand of dQ^T += K^T dS^T (4 steps of 16 keys).
+    u32x4_t sf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool ok = row_ok && key < Nk && (!CAUSAL || key <= my_row + off);
+        const float p = ok ? fast_exp2(__builtin_fmaf(s[kb][e], c, -l2)) : 0.f;
+        x[e] = p * (dp[kb][e] - dl);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        sf[2 * kb + j] = (u32x4_t){pack2<DT>(x[8 * j + 0], x[8 * j + 1]), pack2<DT>(x[8 * j + 2], x[8 * j + 3]),
+                                   pack2<DT>(x[8 * j + 4], x[8 * j + 5]), pack2<DT>(x[8 * j + 6], x[8 * j + 7])};
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sf[ks], dqa[db]);
+  }
+
+  // dQ = scale * (dQ^T)^T: lane row r32, d = 32db + 8(e/4) + 4half + e%4.
+  if (row_ok) {
+    uint16_t* pq = dq + (qrow0 + my_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * half;
+        *reinterpret_cast<u32x2_t*>(pq + d0) =
+            (u32x2_t){pack2<DT>(dqa[db][4 * gq + 0] * scale, dqa[db][4 * gq + 1] * scale),
+                      pack2<DT>(dqa[db][4 * gq + 2] * scale, dqa[db][4 * gq + 3] * scale)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk) {
+  const int64_t a = (int64_t)B * Hkv * ((Nk + kBwdKeysWG - 1) / kBwdKeysWG);
+  const int64_t c = (int64_t)B * Hq * ((Nq + kBwdRowsWG - 1) / kBwdRowsWG);
+  const int64_t r = ((int64_t)B * Hq * Nq + 15) / 16;
+  return a > c ? (a > r ? a : r) : (c > r ? c : r);
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
+                     stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, DT);
+  const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
+                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
+  const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt)),
+                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                     (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+#define MI355_BWD_CASE(DTV, DV)                                              \
+  if (a.dtype == DTV && a.d == DV) {                                         \
+    return a.causal ? launch_bwd_t<DTV, DV, true>(a, stream)                 \
+                    : launch_bwd_t<DTV, DV, false>(a, stream);               \
+  }
+  MI355_BWD_CASE(kBF16, 128)
+  MI355_BWD_CASE(kBF16, 64)
+  MI355_BWD_CASE(kFP16, 128)
+  MI355_BWD_CASE(kFP16, 64)
+#undef MI355_BWD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace mi355attn

@@ -49,13 +49,34 @@ struct CombineArgs {
   int dtype;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nk, d;
+  float scale;
+  int causal;
+  int dtype;
+};
+
 // Number of workgroups the forward launch uses (for the grid-size check).
 int64_t fwd_grid_blocks(int B, int Hq, int Nq);
 // Upper bound on the split kernel's work items (sequence, chunk, kv-head); the
 // kernel indexes them with 32-bit integers.
 int64_t split_work_items(int B, int Hkv, int max_len, int chunk);
 
+// Largest grid of the three backward launches.
+int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk);
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

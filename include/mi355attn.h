@@ -72,6 +72,35 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd — gradients of attn_fwd: given dout = dL/dO, writes dq, dk, dv, with
+ * the probabilities recomputed from the forward's LSE rather than stored (the
+ * backward of the flash-attention page's "flash_bwd_kernel" and the llm.c
+ * page's attention_backward compute the same quantities):
+ *
+ *   D_i = sum_t dout_it o_it,  P_ij = exp(scale q_i.k_j - lse_i) (0 if masked),
+ *   dS_ij = P_ij (dout_i.v_j - D_i),
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,  dv_j = sum_i P_ij dout_i
+ *
+ * where dk and dv of a key/value head sum over the query heads that read it.
+ *
+ *   q, o, dout [B, Hq,  Nq, d]  dtype  (read; o and lse as attn_fwd wrote them)
+ *   k, v       [B, Hkv, Nk, d]  dtype  (read)
+ *   lse        [B, Hq,  Nq]     float  (read)
+ *   delta      [B, Hq,  Nq]     float  (workspace owned by the caller: written
+ *                                       with D, then read)
+ *   dq         [B, Hq,  Nq, d]  dtype  (written, rounded to nearest even)
+ *   dk, dv     [B, Hkv, Nk, d]  dtype  (written, rounded to nearest even)
+ *
+ * Shapes, head mapping, causal alignment, d, dtype and scale as in attn_fwd. A
+ * query row with no allowed key contributes nothing and gets dq = 0. Three
+ * kernels run in order on `stream`; the result does not depend on scheduling
+ * (no atomics).
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
+             int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
+
+/*
  * attn_fwd_varlen — attn_fwd over a packed batch of sequences of different
  * lengths (the variable-length mode that the flash-attention page's kernel
  * traits carry as a flag): no padding, each sequence attends only to its own

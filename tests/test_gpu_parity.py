@@ -411,3 +411,59 @@ def test_fwd_varlen_full_size_sampled():
         og = o[s0 + rows[:, 2], rows[:, 1]]
         lg = lse[rows[:, 1], s0 + rows[:, 2]]
         check(og, lg, ro, rl, "bf16", "varlen full size, sequence %d (N=%d)" % (b, n))
+
+
+# --------------------------------------------------------------- backward
+
+# Gradient tolerance. There is no gate for gradients in the task; the errors
+# come from rounding P and dS to the input dtype before their products (relative
+# 2^-9 for bf16, 2^-12 for fp16 per term) and from rounding the outputs, so the
+# gate is relative to the largest reference gradient of the tensor: bf16 2^-6,
+# fp16 2^-8 (a few output ulps at that magnitude).
+TOL_GRAD = {"bf16": 2.0 ** -6, "fp16": 2.0 ** -8}
+
+BWD = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype, causal
+    (1, 2, 2, 128, 128, 64, "fp16", True),
+    (1, 2, 2, 128, 128, 64, "fp16", False),
+    (2, 4, 2, 200, 200, 128, "bf16", True),
+    (1, 8, 2, 300, 100, 128, "bf16", True),
+    (1, 4, 4, 100, 300, 128, "bf16", True),
+    (1, 4, 1, 257, 257, 64, "bf16", False),
+    (1, 4, 4, 1000, 1000, 128, "bf16", True),
+    (1, 4, 4, 2048, 2048, 128, "bf16", True),
+]
+
+
+def _check_grad(g_gpu, g_ref, dtype, what):
+    g = g_gpu.detach().float().cpu().double().numpy()
+    assert np.isfinite(g).all(), "%s: NaN/Inf" % what
+    err = np.abs(g - g_ref)
+    scale = max(1e-30, np.abs(g_ref).max())
+    print("%s: max err %.3e, max |ref| %.3e, ratio %.3e" % (what, err.max(), scale,
+                                                          err.max() / scale))
+    assert err.max() <= TOL_GRAD[dtype] * scale, "%s: %s" % (what, _report(err, g_ref))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", BWD)
+def test_backward(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    seed = zlib.crc32(repr(("bwd", B, Hq, Hkv, Nq, Nk, d, dtype, causal)).encode()) % 10000
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = ea.fwd(qd, kd, vd, causal=causal, scale=scale)
+    outs = [_guarded(t.shape, t.dtype) for t in (qd, kd, vd)]
+    deltab, delta = _guarded(tuple(lse.shape), torch.float32)
+    ea.attn_bwd(qd, kd, vd, o, dod, lse, delta, outs[0][1], outs[1][1], outs[2][1], causal,
+                scale)
+    torch.cuda.synchronize()
+    for buf, t in outs + [(deltab, delta)]:
+        assert _guard_ok(buf, t.numel()), "write outside an output"
+    rq, rk, rv = oracle.attn_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do),
+                                 wl.DTYPE_CODE[dtype], scale, causal)
+    tag = "bwd %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, causal),)
+    _check_grad(outs[0][1], rq, dtype, tag + " dq")
+    _check_grad(outs[1][1], rk, dtype, tag + " dk")
+    _check_grad(outs[2][1], rv, dtype, tag + " dv")
