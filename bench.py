@@ -14,6 +14,7 @@ Prints ONE JSON line:
                 the forward's flops, timed in a loop of its own
   fwd_varlen    a packed causal prefill batch (8192 tokens in sequences of seeded
                 lengths U[256, 4096]), TFLOP/s, timed in a loop of its own
+  decode_auto   the same decode through attn_decode (the library's chunk length)
   decode_paged  the same decode over a paged cache (64-row pages, shuffled pool,
                 block tables), timed in a loop of its own after the steps
   roofline    the forward kernel against the bf16 dense MFMA peak
@@ -54,6 +55,8 @@ def parse():
                     help="skip the backward measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement")
+    ap.add_argument("--no-auto", action="store_true",
+                    help="skip the one-call decode (library chunk) measurement")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
@@ -189,6 +192,40 @@ def cpu_baseline(w, q, k, v, target_s):
 
 
 PAGE_SIZE = 64
+
+
+def bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc, stream):
+    """attn_decode on the decode workload: the library picks the chunk length (2048
+    keys here) instead of the workload's 512. Timed in a loop of its own."""
+    print("bench: one-call decode", file=sys.stderr, flush=True)
+    B, Hq, d = dq.shape
+    n = ea.attn_decode_workspace(B, Hq, kc.shape[1], kc.shape[2], d)
+    ws = torch.empty((n,), dtype=torch.float32, device=dq.device) if n else None
+    o = torch.empty((B, Hq, d), dtype=dq.dtype, device=dq.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dq.device)
+
+    def run():
+        ea.attn_decode(dq, kc, vc, sld, o, lse, ws, wd.scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    lens = sl.numpy().astype(np.int64)
+    kv_bytes = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    slots = n // (B * Hq * (d + 1)) if n else 1  # chunk slots per (b, h)
+    return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4),
+            "chunk_slots": slots, "chunk": -(-kc.shape[2] // slots), "workspace_floats": n,
+            "roofline": {"kernel": "attn_decode_split_kernel + combine (library chunk)",
+                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
 VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX = 8192, 256, 4096
 
 
@@ -427,6 +464,9 @@ def main():
         out["bwd"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream)
     if do_pre and not args.no_varlen:
         out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
+    if do_dec and not args.no_auto:
+        out["decode_auto"] = bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc,
+                                               stream)
     if do_dec and not args.no_paged:
         out["decode_paged"] = bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc,
                                           stream)

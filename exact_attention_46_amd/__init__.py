@@ -12,13 +12,16 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     attn_bwd,
+    attn_decode,
     attn_decode_combine,
     attn_decode_split,
     attn_decode_split_paged,
+    attn_decode_workspace,
     attn_fwd,
     attn_fwd_varlen,
     attn_status_str,
     decode,
+    decode_auto,
     decode_buffers,
     decode_paged,
     default_scale,

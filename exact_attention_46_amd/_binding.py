@@ -28,7 +28,8 @@ ERR_BAD_ARG = -5
 ERR_HIP = -6
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_decode_split",
-           "attn_decode_split_paged", "attn_decode_combine", "attn_status_str")
+           "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
+           "attn_decode_workspace", "attn_status_str")
 
 _DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 
@@ -53,6 +54,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
         lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
+        ll = ctypes.c_longlong
+        lib.attn_decode.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, f, i, p]
+        lib.attn_decode_workspace.argtypes = [i, i, i, i, i]
         lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
         lib.attn_decode_split_paged.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f,
                                                 i, p]
@@ -61,6 +65,8 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_varlen.restype = i
         lib.attn_bwd.restype = i
+        lib.attn_decode.restype = i
+        lib.attn_decode_workspace.restype = ctypes.c_longlong
         lib.attn_decode_split.restype = i
         lib.attn_decode_split_paged.restype = i
         lib.attn_decode_combine.restype = i
@@ -297,4 +303,52 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, chunk: int = 512,
     attn_decode_split_paged(q, k_pages, v_pages, block_table, seq_lens, part_o, part_lse, chunk,
                             scale, stream)
     attn_decode_combine(part_o, part_lse, seq_lens, o, lse, chunk, stream)
+    return o, lse
+
+
+def attn_decode_workspace(B: int, Hq: int, Hkv: int, max_len: int, d: int) -> int:
+    """Floats of workspace attn_decode needs (0 for a single pass); raises on a bad shape."""
+    n = load_library().attn_decode_workspace(B, Hq, Hkv, max_len, d)
+    if n < 0:
+        raise AttnError("attn_decode_workspace", int(n))
+    return int(n)
+
+
+def attn_decode(q, k_cache, v_cache, seq_lens, o, lse, workspace, scale: float,
+                stream=None) -> None:
+    """Calls attn_decode. workspace: fp32 tensor on the GPU (or None when none is needed)."""
+    ts = [q, k_cache, v_cache, seq_lens, o, lse] + ([workspace] if workspace is not None else [])
+    _gpu(*ts)
+    B, Hq, d = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    _need(v_cache.shape == k_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d,
+          "cache shapes")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and o.dtype == q.dtype,
+          "dtypes differ")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens [B] int32")
+    _need(tuple(o.shape) == (B, Hq, d), "o [B,Hq,d]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq), "lse [B,Hq] fp32")
+    if workspace is not None:
+        _need(workspace.dtype == torch.float32, "workspace must be fp32")
+    wp = _ptr(workspace) if workspace is not None else None
+    wn = workspace.numel() if workspace is not None else 0
+    st = load_library().attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                    _ptr(o), _ptr(lse), wp, wn, B, Hq, Hkv, max_len, d,
+                                    float(scale), _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode", st)
+
+
+def decode_auto(q, k_cache, v_cache, seq_lens, scale: float | None = None, stream=None,
+                workspace=None):
+    """One-call decode with the library's chunk choice. Returns (o, lse)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    B, Hq, d = q.shape
+    if workspace is None:
+        n = attn_decode_workspace(B, Hq, k_cache.shape[1], k_cache.shape[2], d)
+        workspace = torch.empty((n,), dtype=torch.float32, device=q.device) if n else None
+    o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    attn_decode(q, k_cache, v_cache, seq_lens, o, lse, workspace, scale, stream)
     return o, lse

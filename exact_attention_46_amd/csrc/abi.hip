@@ -135,6 +135,67 @@ extern "C" int attn_decode_split_paged(const void* q, const void* k_pages, const
   return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Shared checks of attn_decode and attn_decode_workspace (everything but pointers).
+int decode_shape_status(int B, int Hq, int Hkv, int max_len, int d) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || max_len > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || Hq / Hkv > 32) return MI355ATTN_ERR_UNSUPPORTED;
+  return MI355ATTN_OK;
+}
+
+int64_t decode_workspace_floats(int B, int Hq, int Hkv, int max_len, int d, int* chunk_out) {
+  const int chunk = mi355attn::decode_chunk_policy(B, Hkv, max_len);
+  if (chunk_out) *chunk_out = chunk;
+  if (chunk >= max_len) return 0;
+  const int64_t C = ((int64_t)max_len + chunk - 1) / chunk;
+  return (int64_t)B * Hq * C * (d + 1);
+}
+
+}  // namespace
+
+extern "C" long long attn_decode_workspace(int B, int Hq, int Hkv, int max_len, int d) {
+  const int st = decode_shape_status(B, Hq, Hkv, max_len, d);
+  if (st != MI355ATTN_OK) return st;
+  return decode_workspace_floats(B, Hq, Hkv, max_len, d, nullptr);
+}
+
+extern "C" int attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                           const int* seq_lens, void* o, float* lse, float* workspace,
+                           long long workspace_floats, int B, int Hq, int Hkv, int max_len, int d,
+                           float scale, int dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !seq_lens || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
+  const int st = decode_shape_status(B, Hq, Hkv, max_len, d);
+  if (st != MI355ATTN_OK) return st;
+  if (!dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 16))
+    return MI355ATTN_ERR_MISALIGNED;
+  int chunk = 0;
+  const int64_t need = decode_workspace_floats(B, Hq, Hkv, max_len, d, &chunk);
+  if (need > 0 && (!workspace || workspace_floats < need)) return MI355ATTN_ERR_BAD_ARG;
+  if (mi355attn::split_work_items(B, Hkv, max_len, chunk) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (need == 0) {  // one chunk per sequence: the split kernel writes the result
+    mi355attn::SplitArgs a{q, k_cache, v_cache, seq_lens, nullptr, nullptr, B, Hq, Hkv, max_len,
+                           d, chunk, scale, dtype};
+    a.o_final = o;
+    a.lse_final = lse;
+    return from_hip(mi355attn::launch_split(a, s));
+  }
+  const int C = (int)(((int64_t)max_len + chunk - 1) / chunk);
+  float* part_o = workspace;
+  float* part_lse = workspace + (int64_t)B * Hq * C * d;
+  mi355attn::SplitArgs a{q, k_cache, v_cache, seq_lens, part_o, part_lse, B, Hq, Hkv, max_len,
+                         d, chunk, scale, dtype};
+  const int rc = from_hip(mi355attn::launch_split(a, s));
+  if (rc != MI355ATTN_OK) return rc;
+  mi355attn::CombineArgs c{part_o, part_lse, seq_lens, o, lse, B, Hq, C, d, chunk, dtype};
+  return from_hip(mi355attn::launch_combine(c, s));
+}
+
 extern "C" int attn_decode_combine(const float* part_o, const float* part_lse,
                                    const int* seq_lens, void* o, float* lse, int B, int Hq,
                                    int max_chunks, int d, int chunk, int dtype, void* stream) {

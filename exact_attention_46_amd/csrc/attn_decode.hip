@@ -112,12 +112,17 @@ struct PagedKV {
   int page_size, max_pages, num_pages;
 };
 
-template <int DT, int D, bool PAGED>
+// FINAL: every sequence fits one chunk (chunk >= max_len), so each item's
+// normalised output is the final one: it is written rounded to the input dtype
+// into o [B, Hq, d] and its LSE into lse [B, Hq], and no combine is needed
+// (sequences of length 0 get O = 0, LSE = -inf).
+template <int DT, int D, bool PAGED, bool FINAL>
 __global__ void __launch_bounds__(kSplitThreads, 1)
 attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                          const uint16_t* __restrict__ vc, const int* __restrict__ seq_lens,
                          float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq,
-                         int Hkv, int max_len, int chunk, int C, float scale, PagedKV pk) {
+                         int Hkv, int max_len, int chunk, int C, float scale, PagedKV pk,
+                         uint16_t* __restrict__ o_fin, float* __restrict__ lse_fin) {
   using Lay = SplitLayout<D>;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
@@ -135,12 +140,24 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int gwave = blockIdx.x * kSplitWaves + wave;
   const int nwaves = gridDim.x * kSplitWaves;
 
-  // Chunk slots past the end of a sequence: LSE = -inf (O is not written).
-  for (int64_t i = (int64_t)blockIdx.x * kSplitThreads + tid; i < (int64_t)B * Hq * C;
-       i += (int64_t)gridDim.x * kSplitThreads) {
-    const int cc = (int)(i % C);
-    const int bb = (int)(i / ((int64_t)Hq * C));
-    if (cc >= chunks_of(seq_lens, bb, max_len, chunk)) part_lse[i] = -INFINITY;
+  if constexpr (FINAL) {
+    // Empty sequences: O = 0, LSE = -inf (no item covers them).
+    for (int64_t i = (int64_t)blockIdx.x * kSplitThreads + tid; i < (int64_t)B * Hq;
+         i += (int64_t)gridDim.x * kSplitThreads) {
+      if (chunks_of(seq_lens, (int)(i / Hq), max_len, chunk) == 0) {
+        lse_fin[i] = -INFINITY;
+        for (int t = 0; t < D; t += 8)
+          *reinterpret_cast<u32x4_t*>(o_fin + i * D + t) = (u32x4_t){0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
+    // Chunk slots past the end of a sequence: LSE = -inf (O is not written).
+    for (int64_t i = (int64_t)blockIdx.x * kSplitThreads + tid; i < (int64_t)B * Hq * C;
+         i += (int64_t)gridDim.x * kSplitThreads) {
+      const int cc = (int)(i % C);
+      const int bb = (int)(i / ((int64_t)Hq * C));
+      if (cc >= chunks_of(seq_lens, bb, max_len, chunk)) part_lse[i] = -INFINITY;
+    }
   }
 
   const int n_items =
@@ -285,7 +302,8 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   bool pend = false;
   f32x16_t opend[DB];
   float* pend_dst = part_o;
-  float* pend_lse = part_lse;
+  uint16_t* pend_fin = o_fin;
+  float* pend_lse = FINAL ? lse_fin : part_lse;
   float pend_lse_val = 0.f;
   // Exactly NS vector-memory stores (lanes 0 and 32 always take part).
   auto store_pending = [&]() {
@@ -295,11 +313,17 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int d0 = db * 32 + 8 * gq + 4 * half;
-          // The combine reads the partials once, later: stream them past
-          // the caches instead of holding KV lines' space for them.
-          __builtin_nontemporal_store((f32x4_t){opend[db][4 * gq + 0], opend[db][4 * gq + 1],
-                                                opend[db][4 * gq + 2], opend[db][4 * gq + 3]},
-                                      reinterpret_cast<f32x4_t*>(pend_dst + d0));
+          if constexpr (FINAL) {
+            *reinterpret_cast<u32x2_t*>(pend_fin + d0) =
+                (u32x2_t){pack2<DT>(opend[db][4 * gq + 0], opend[db][4 * gq + 1]),
+                          pack2<DT>(opend[db][4 * gq + 2], opend[db][4 * gq + 3])};
+          } else {
+            // The combine reads the partials once, later: stream them past
+            // the caches instead of holding KV lines' space for them.
+            __builtin_nontemporal_store((f32x4_t){opend[db][4 * gq + 0], opend[db][4 * gq + 1],
+                                                  opend[db][4 * gq + 2], opend[db][4 * gq + 3]},
+                                        reinterpret_cast<f32x4_t*>(pend_dst + d0));
+          }
         }
       if (half == 0) __builtin_nontemporal_store(pend_lse_val, pend_lse);
     }
@@ -434,8 +458,13 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       const int64_t row = (int64_t)cur.b * Hq + (int64_t)cur.g * R + (r32 < R ? r32 : 0);
       const bool empty = !(l_row > 0.f);
       const float inv = empty ? 0.f : 1.f / lr_row;
-      pend_dst = part_o + (row * C + cur.c) * D;
-      pend_lse = part_lse + row * C + cur.c;
+      if constexpr (FINAL) {
+        pend_fin = o_fin + row * D;
+        pend_lse = lse_fin + row;
+      } else {
+        pend_dst = part_o + (row * C + cur.c) * D;
+        pend_lse = part_lse + row * C + cur.c;
+      }
       pend_lse_val = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
 #pragma unroll
       for (int db = 0; db < DB; ++db) opend[db] = oacc[db] * inv;
@@ -550,21 +579,45 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Chunk length for attn_decode: enough work items (about eight per resident
+// wave when every sequence had max_len keys) to balance sequences of unequal
+// length, without chunks so short that the partials and the combine dominate
+// (measured on gfx950: 2048-key chunks stream the 64-sequence, L ~ U[512, 32768]
+// decode at 6.5 TB/s against 6.0 with 512). Returns max_len (one pass, no
+// combine) when that many (sequence, kv-head) items already fill the waves.
+int decode_chunk_policy(int B, int Hkv, int max_len) {
+  const int64_t waves = (int64_t)device_cus() * kSplitWaves;
+  if (max_len <= 2048 && (int64_t)B * Hkv >= waves) return max_len;
+  int64_t c = (int64_t)B * Hkv * max_len / (8 * waves);
+  int chunk = 256;
+  while (chunk < 2048 && 2 * chunk <= c) chunk *= 2;
+  return max_len <= chunk ? max_len : chunk;
+}
+
 template <int DT, int D>
 static hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   const int max_len = a.block_table ? a.max_pages * a.page_size : a.max_len;
   const int C = (int)(((int64_t)max_len + a.chunk - 1) / a.chunk);
   const PagedKV pk{a.block_table, a.page_size, a.max_pages, a.num_pages};
+  uint16_t* o_fin = (uint16_t*)a.o_final;
   if (a.block_table) {
-    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, true>), dim3((unsigned)device_cus()),
+    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, true, false>), dim3((unsigned)device_cus()),
                        dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk);
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
+                       o_fin, a.lse_final);
+  } else if (a.o_final) {
+    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false, true>), dim3((unsigned)device_cus()),
+                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
+                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
+                       o_fin, a.lse_final);
   } else {
-    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false>), dim3((unsigned)device_cus()),
+    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false, false>), dim3((unsigned)device_cus()),
                        dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
                        (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk);
+                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
+                       o_fin, a.lse_final);
   }
   return hipGetLastError();
 }

@@ -37,6 +37,9 @@ struct SplitArgs {
   // [num_pages, page_size, Hkv, d] and max_len is max_pages * page_size.
   const int* block_table = nullptr;
   int page_size = 0, max_pages = 0, num_pages = 0;
+  // One pass (chunk >= max_len): final O [B, Hq, d] (dtype) and LSE [B, Hq].
+  void* o_final = nullptr;
+  float* lse_final = nullptr;
 };
 
 struct CombineArgs {
@@ -71,6 +74,8 @@ int64_t fwd_grid_blocks(int B, int Hq, int Nq);
 // Upper bound on the split kernel's work items (sequence, chunk, kv-head); the
 // kernel indexes them with 32-bit integers.
 int64_t split_work_items(int B, int Hkv, int max_len, int chunk);
+// Chunk length attn_decode uses for this shape (max_len: one pass).
+int decode_chunk_policy(int B, int Hkv, int max_len);
 
 // Largest grid of the three backward launches.
 int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk);

@@ -210,6 +210,40 @@ int attn_decode_combine(const float* part_o, const float* part_lse, const int* s
                         void* o, float* lse, int B, int Hq, int max_chunks, int d, int chunk,
                         int dtype, void* stream);
 
+/*
+ * attn_decode — single-token decode in one call: the library picks the chunk
+ * length from the shape and runs attn_decode_split (+ attn_decode_combine) with
+ * it, or, when one chunk covers max_len and the (sequence, kv-head) pairs
+ * already fill the GPU, a single pass whose split kernel writes o and lse
+ * itself (no partials, no combine; the unsplit short-context regime of the
+ * abaddon page's cached-decode kernel, done with one read of K and V and no
+ * atomics). The chunk is about eight work items per resident wave if every
+ * sequence had max_len keys, clamped to [256, 2048] keys.
+ *
+ *   q, k_cache, v_cache, seq_lens  as attn_decode_split
+ *   o          [B, Hq, d]   dtype  (written, rounded to nearest even)
+ *   lse        [B, Hq]      float  (written)
+ *   workspace  float array of workspace_floats elements, 16-byte aligned,
+ *              owned by the caller; it must hold at least
+ *              attn_decode_workspace(B, Hq, Hkv, max_len, d) floats (NULL is
+ *              allowed when that is 0). Its contents are scratch.
+ *
+ * The result equals attn_decode_split + attn_decode_combine at any chunk (up to
+ * rounding). A too-small workspace returns MI355ATTN_ERR_BAD_ARG.
+ */
+int attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* seq_lens,
+                void* o, float* lse, float* workspace, long long workspace_floats, int B, int Hq,
+                int Hkv, int max_len, int d, float scale, int dtype, void* stream);
+
+/*
+ * attn_decode_workspace — the number of floats attn_decode needs as workspace
+ * for this shape on the current device (0: a single pass needs none), or a
+ * negative status code for a shape attn_decode would reject. The chunk choice
+ * depends on the device's compute-unit count, so query it on the device that
+ * will run the decode.
+ */
+long long attn_decode_workspace(int B, int Hq, int Hkv, int max_len, int d);
+
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);
 

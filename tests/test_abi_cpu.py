@@ -21,7 +21,8 @@ MIS = ctypes.c_void_p(4098)
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:const\s+)?(?:long\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text,
+                      flags=re.M)
 
 
 def header_defines():
@@ -136,6 +137,28 @@ def split_paged(lib, q=A, kp=A, vp=A, bt=A2, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv
 ])
 def test_attn_decode_split_paged_rejects(lib, kw, code):
     assert split_paged(lib, **kw) == code
+
+
+def decode_one(lib, q=A, kc=A, vc=A, sl=A2, o=A, lse=A2, ws=A, wn=1 << 30, B=2, Hq=8, Hkv=2,
+               max_len=64, d=128, scale=0.1, dtype=0):
+    return lib.attn_decode(q, kc, vc, sl, o, lse, ws, wn, B, Hq, Hkv, max_len, d, scale, dtype,
+                           None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(sl=None), -1),
+    (dict(B=0), -2), (dict(max_len=0), -2), (dict(Hq=6, Hkv=4), -2), (dict(max_len=2**23 + 1), -2),
+    (dict(d=80), -3), (dict(dtype=5), -3), (dict(Hq=66, Hkv=2), -3),
+    (dict(scale=0.0), -5), (dict(kc=MIS), -4), (dict(ws=MIS), -4),
+])
+def test_attn_decode_rejects(lib, kw, code):
+    assert decode_one(lib, **kw) == code
+
+
+def test_attn_decode_workspace_rejects_bad_shapes(lib):
+    assert lib.attn_decode_workspace(0, 8, 2, 64, 128) == -2
+    assert lib.attn_decode_workspace(2, 8, 2, 64, 96) == -3
+    assert lib.attn_decode_workspace(2, 6, 4, 64, 128) == -2
 
 
 def combine(lib, po=A, pl=A2, sl=A2, o=A, lse=A2, B=2, Hq=8, C=4, d=128, chunk=16, dtype=0):

@@ -467,3 +467,58 @@ def test_backward(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     _check_grad(outs[0][1], rq, dtype, tag + " dq")
     _check_grad(outs[1][1], rk, dtype, tag + " dk")
     _check_grad(outs[2][1], rv, dtype, tag + " dv")
+
+
+# --------------------------------------------------------------- one-call decode (library chunk)
+
+AUTO = [
+    # B, Hq, Hkv, d, dtype, lens (None: drawn on [1, max_len]), max_len
+    (256, 32, 8, 128, "bf16", None, 512),        # one pass: 2048 items fill the waves
+    (64, 32, 8, 128, "bf16", None, 512),         # split into 256-key chunks + combine
+    (300, 8, 8, 64, "fp16", [0, 1, 300] * 100, 300),  # one pass, empty sequences included
+    (16, 32, 8, 128, "bf16", None, 2048),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dtype,lens,max_len", AUTO)
+def test_decode_one_call(B, Hq, Hkv, d, dtype, lens, max_len):
+    seed = 3000 + B + max_len + d
+    sl, q, kc, vc = wl.decode_inputs(B, Hq, Hkv, d, dtype, seed, l_min=1, l_max=max_len,
+                                     max_len=max_len, device="cpu", seq_lens=lens)
+    scale = 1.0 / math.sqrt(d)
+    qd, kcd, vcd, sld = _dev(q, kc, vc, sl)
+    n = ea.attn_decode_workspace(B, Hq, Hkv, max_len, d)
+    wsb, ws = _guarded((max(n, 1),), torch.float32)
+    ob, o = _guarded((B, Hq, d), q.dtype)
+    lb, lse = _guarded((B, Hq), torch.float32)
+    ea.attn_decode(qd, kcd, vcd, sld, o, lse, ws if n else None, scale)
+    torch.cuda.synchronize()
+    for buf, t in ((wsb, ws), (ob, o), (lb, lse)):
+        assert _guard_ok(buf, t.numel()), "write outside an output or the workspace"
+    ro, rl = oracle.decode(wl.bits(q), wl.bits(kc), wl.bits(vc), sl.numpy(), wl.DTYPE_CODE[dtype],
+                           scale)
+    check(o, lse, ro, rl, dtype, "one-call decode (workspace %d floats)" % n)
+
+
+def test_decode_one_call_workspace_sizes():
+    # decode workload: 2048-key chunks -> 16 chunk slots; short batch: one pass
+    assert ea.attn_decode_workspace(64, 32, 8, 32768, 128) == 64 * 32 * 16 * 129
+    assert ea.attn_decode_workspace(256, 32, 8, 512, 128) == 0
+    with pytest.raises(ea.AttnError):
+        ea.attn_decode_workspace(2, 6, 4, 64, 128)
+
+
+def test_decode_one_call_full_size_sampled():
+    w = wl.WORKLOADS["decode"]
+    sl, q, kc, vc = wl.workload_decode_inputs(w, device="cuda")
+    qd, sld = q.cuda(), sl.cuda()
+    o, lse = ea.decode_auto(qd, kc, vc, sld, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    lens = sl.numpy()
+    for b in sorted({int(np.argmax(lens)), int(np.argmin(lens)), 7, 50}):
+        L = int(lens[b])
+        ro, rl = oracle.decode(wl.bits(q[b:b + 1]), wl.bits(kc[b:b + 1, :, :L].cpu()),
+                               wl.bits(vc[b:b + 1, :, :L].cpu()), np.array([L], dtype=np.int32),
+                               0, w.scale)
+        check(o[b:b + 1], lse[b:b + 1], ro, rl, "bf16", "one-call decode seq %d (L=%d)" % (b, L))
