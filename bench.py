@@ -12,6 +12,7 @@ Prints ONE JSON line:
   decode      KV GB/s = sum_b 2*Hkv*L_b*d*2 bytes / mean (split + combine) time
   bwd           the backward (dQ, dK, dV) on the prefill workload, TFLOP/s at 2.5x
                 the forward's flops, timed in a loop of its own
+  fwd_local     sliding-window attention (512 keys back) on the prefill shapes
   fwd_varlen    a packed causal prefill batch (8192 tokens in sequences of seeded
                 lengths U[256, 4096]), TFLOP/s, timed in a loop of its own
   decode_auto   the same decode through attn_decode (the library's chunk length)
@@ -53,6 +54,8 @@ def parse():
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-bwd", action="store_true",
                     help="skip the backward measurement")
+    ap.add_argument("--no-local", action="store_true",
+                    help="skip the sliding-window measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement")
     ap.add_argument("--no-auto", action="store_true",
@@ -263,6 +266,40 @@ def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
+LOCAL_WINDOW = 512
+
+
+def bench_local(args, torch, np, ea, wp, qg, kg, vg, stream):
+    """Sliding-window attention on the llm_prefill shapes: each row sees its own
+    key and the LOCAL_WINDOW keys before it. TFLOP/s counts 4*d flops per allowed
+    (row, key) pair. Timed in a loop of its own after the steps."""
+    print("bench: sliding-window attention", file=sys.stderr, flush=True)
+    o = torch.empty_like(qg)
+    lse = torch.empty(qg.shape[:3], dtype=torch.float32, device=qg.device)
+
+    def run():
+        ea.attn_fwd_local(qg, kg, vg, o, lse, LOCAL_WINDOW, 0, wp.scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    pairs = float(sum(min(i, LOCAL_WINDOW) + 1 for i in range(wp.N)))
+    flops = 4.0 * wp.B * wp.Hq * wp.d * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "window": [LOCAL_WINDOW, 0],
+            "roofline": {"kernel": "attn_fwd_kernel<bf16,128,local>", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def bench_varlen(args, torch, np, ea, wl, dev, stream):
     """A packed causal prefill batch with the llm_prefill token budget (8192 tokens,
     Hq = Hkv = 32, d = 128, bf16) split into sequences of seeded lengths
@@ -462,6 +499,8 @@ def main():
                                       "traffic": load_traffic("attn_decode_split_kernel/decode")}}
     if do_pre and not args.no_bwd:
         out["bwd"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream)
+    if do_pre and not args.no_local:
+        out["fwd_local"] = bench_local(args, torch, np, ea, wp, qg, kg, vg, stream)
     if do_pre and not args.no_varlen:
         out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
     if do_dec and not args.no_auto:

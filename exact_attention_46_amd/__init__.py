@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     attn_decode_split_paged,
     attn_decode_workspace,
     attn_fwd,
+    attn_fwd_local,
     attn_fwd_varlen,
     attn_status_str,
     decode,
@@ -26,6 +27,7 @@ from ._binding import (  # noqa: F401
     decode_paged,
     default_scale,
     fwd,
+    fwd_local,
     fwd_varlen,
     load_library,
 )

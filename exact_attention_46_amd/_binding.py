@@ -27,7 +27,7 @@ ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_bwd", "attn_decode_split",
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_bwd", "attn_decode_split",
            "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
            "attn_decode_workspace", "attn_status_str")
 
@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
+        lib.attn_fwd_local.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, i, p]
         lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         ll = ctypes.c_longlong
         lib.attn_decode.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, f, i, p]
@@ -64,6 +65,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_status_str.argtypes = [i]
         lib.attn_fwd.restype = i
         lib.attn_fwd_varlen.restype = i
+        lib.attn_fwd_local.restype = i
         lib.attn_bwd.restype = i
         lib.attn_decode.restype = i
         lib.attn_decode_workspace.restype = ctypes.c_longlong
@@ -124,6 +126,35 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                                  _stream(stream))
     if st != OK:
         raise AttnError("attn_fwd", st)
+
+
+def attn_fwd_local(q, k, v, o, lse, window_left: int, window_right: int, scale: float,
+                   stream=None) -> None:
+    """Calls attn_fwd_local (shapes as attn_fwd; a negative window bound is no bound)."""
+    _gpu(q, k, v, o, lse)
+    _need(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D, k ~ v")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape[0] == B and k.shape[3] == d, "k/v batch or head dim differ from q")
+    _need(k.dtype == q.dtype and v.dtype == q.dtype and o.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape, "o must have q's shape")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq, Nq), "lse [B,Hq,Nq] fp32")
+    st = load_library().attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv,
+                                       Nq, Nk, d, float(scale), int(window_left),
+                                       int(window_right), _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_fwd_local", st)
+
+
+def fwd_local(q, k, v, window_left: int, window_right: int = 0, scale: float | None = None,
+              stream=None):
+    """Allocates and returns (o, lse) for sliding-window attention."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    attn_fwd_local(q, k, v, o, lse, window_left, window_right, scale, stream)
+    return o, lse
 
 
 def attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool, scale: float,

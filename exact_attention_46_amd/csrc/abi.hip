@@ -39,6 +39,28 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int attn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                              int window_left, int window_right, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (Hq % Hkv != 0 || Nq > kMaxSeq || Nk > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::fwd_grid_blocks(B, Hq, Nq) > kMaxGrid || (int64_t)B * Hq > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  // Bounds beyond the key range are no bounds (keeps the kernel's int arithmetic small).
+  const int wl = window_left < 0 || window_left >= kMaxSeq * 2 ? -1 : window_left;
+  const int wr = window_right < 0 || window_right >= kMaxSeq * 2 ? -1 : window_right;
+  mi355attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, 0, dtype};
+  a.local = true;
+  a.window_left = wl;
+  a.window_right = wr;
+  return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, float* delta, void* dq, void* dk,
                         void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,

@@ -51,6 +51,8 @@
 // them. Each product runs as one dependent MFMA chain per accumulator block
 // (all steps of S block 0, then block 1; all key steps of each O block), 2-3%
 // faster on gfx950 than interleaving the blocks.
+#include <climits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -137,16 +139,26 @@ struct VarLen {
   int total_q, total_k;
 };
 
+// Local (sliding-window) attention: key j is allowed for query row i iff
+// i + off - left <= j <= i + off + right (off = Nk - Nq); a negative bound is
+// no bound on that side, so (left, right) = (-1, 0) is the causal mask.
+struct Window {
+  int left, right;
+};
+
 // VARLEN = false: dense [B, H, N, d] tensors of Nq / Nk rows per head.
 // VARLEN = true: packed batches (see VarLen); Nq / Nk are then the largest
 // sequence lengths, which size the grid, and each workgroup takes its
 // sequence's own lengths (workgroups past the end of a sequence exit).
-template <int DT, int D, bool CAUSAL, bool VARLEN>
+// LOCAL = true: the mask is the window `win` (CAUSAL is false then); each
+// workgroup walks only the key tiles its rows' windows touch, and each wave
+// only the range of them its own rows touch.
+template <int DT, int D, bool CAUSAL, bool VARLEN, bool LOCAL>
 __global__ void __launch_bounds__(kFwdThreads, 1)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                 float* __restrict__ lse, int B, int Hq, int Hkv, int Nq, int Nk, float scale,
-                VarLen vl) {
+                VarLen vl, Window win) {
   using Lay = FwdLayout<D>;
   constexpr int DS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -204,12 +216,19 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const auto rq = VARLEN ? make_rsrc(qh + (int64_t)q0 * QS, (uint32_t)(q_rows - 1) * QS * 2 + ROW)
                          : make_rsrc(qh, (uint32_t)Nq * ROW);
 
-  // Keys this workgroup can see: [0, kv_end).
+  // Keys this workgroup can see: [kv_begin, kv_end); its tiles t0 .. n_tiles-1.
   int kv_end = Nk;
   if (CAUSAL) {
     kv_end = min(q0 + kFwdBM, Nq) - 1 + off + 1;
     kv_end = max(0, min(kv_end, Nk));
   }
+  int kv_begin = 0;
+  if constexpr (LOCAL) {
+    if (win.right >= 0) kv_end = max(0, min(Nk, min(q0 + kFwdBM, Nq) - 1 + off + win.right + 1));
+    if (win.left >= 0) kv_begin = max(0, q0 + off - win.left);
+    if (kv_begin > kv_end) kv_begin = kv_end;
+  }
+  const int t0 = LOCAL ? kv_begin / kFwdBN : 0;
   const int n_tiles = (kv_end + kFwdBN - 1) / kFwdBN;
 
   // ---- Q: the wave's 32 rows go HBM -> its own LDS block once, swizzled like
@@ -296,7 +315,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
 
   // Largest key index this row may see (may be negative: then nothing).
-  const int row_kmax = CAUSAL ? min(my_row + off, Nk - 1) : Nk - 1;
+  int row_kmax = CAUSAL ? min(my_row + off, Nk - 1) : Nk - 1;
+  int row_kmin = 0;  // LOCAL: smallest key index this row may see
+  if constexpr (LOCAL) {
+    if (win.right >= 0) row_kmax = min(my_row + off + win.right, Nk - 1);
+    row_kmin = win.left >= 0 ? my_row + off - win.left : INT_MIN / 2;
+  }
   const bool wave_rows_valid = qw0 < Nq;
   const int wave_last_row = min(qw0 + 31, Nq - 1);
 
@@ -356,14 +380,21 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int k0 = t * kFwdBN;
     // Mask keys past the end and (causal) keys after the row's limit.
     // Element e of block kb holds key k0 + 32*kb + 4*half + 8*(e/4) + e%4.
-    const bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
+    bool need_mask = (k0 + kFwdBN > Nk) || (CAUSAL && k0 + kFwdBN - 1 > qw0 + off);
+    if constexpr (LOCAL)
+      need_mask = need_mask || (win.right >= 0 && k0 + kFwdBN - 1 > qw0 + off + win.right) ||
+                  (win.left >= 0 && k0 < wave_last_row + off - win.left);
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int lim = row_kmax - (k0 + kb * 32 + 4 * half);
+        const int lim_lo = row_kmin - (k0 + kb * 32 + 4 * half);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          s[kb][e] = (8 * (e >> 2) + (e & 3) > lim) ? -INFINITY : s[kb][e];
+        for (int e = 0; e < 16; ++e) {
+          const int ke = 8 * (e >> 2) + (e & 3);
+          const bool out = LOCAL ? (ke > lim || ke < lim_lo) : (ke > lim);
+          s[kb][e] = out ? -INFINITY : s[kb][e];
+        }
       }
     }
 
@@ -445,15 +476,25 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   };
 
-  // Tiles active for this wave (some row may see key 64t) form a prefix.
+  // Tiles active for this wave (some row may see a key of tile t) form the
+  // range [a_lo, n_act) (a prefix, a_lo = 0, unless LOCAL).
   int n_act = 0;
+  int a_lo = 0;
   if (wave_rows_valid) {
     n_act = n_tiles;
     if (CAUSAL) {
       const int last_key = wave_last_row + off;  // keys up to here are visible
       n_act = last_key < 0 ? 0 : min(n_tiles, last_key / kFwdBN + 1);
     }
+    if constexpr (LOCAL) {
+      int hi = Nk, lo = 0;
+      if (win.right >= 0) hi = max(0, min(Nk, wave_last_row + off + win.right + 1));
+      if (win.left >= 0) lo = max(0, qw0 + off - win.left);
+      n_act = hi > lo ? (hi + kFwdBN - 1) / kFwdBN : t0;
+      a_lo = hi > lo ? lo / kFwdBN : t0;
+    }
   }
+  auto active = [&](int t) -> bool { return (LOCAL ? t >= a_lo : true) && t < n_act; };
 
   // Prologue: K(0), V(0), K(1) and the wave's Q rows in flight; S(0) once they
   // land; group A also takes the softmax of S(0). The barrier after that frees
@@ -462,11 +503,11 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // both pass the same barriers.
   f32x16_t st[2];  // S of the next tile to take through the softmax
   u32x4_t pf[4];   // P of the next tile to multiply with V
-  if (n_tiles > 0) {
-    issue_k(0);
-    issue_v(0);
+  if (n_tiles > t0) {
+    issue_k(t0);
+    issue_v(t0);
   }
-  if (n_tiles > 1) issue_k(1);
+  if (n_tiles > t0 + 1) issue_k(t0 + 1);
   issue_q();
   wait_all_memory();
   __syncthreads();
@@ -492,32 +533,32 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // goes first and the softmax of the partner fills the cycles in between
   // (1.5-2% faster on gfx950 across causal and non-causal shapes).
   auto matrix_phase = [&](int t) {
-    const bool act = t < n_act, act_next = t + 1 < n_act;
+    const bool act = active(t), act_next = active(t + 1);
     __builtin_amdgcn_s_setprio(1);
     if (act_next) qk(t + 1, st, act, t);
     if (act) pv(t, pf, act_next);
     __builtin_amdgcn_s_setprio(0);
   };
   if (!role_b) {
-    if (n_act > 0) {
-      qk(0, st, false, 0);
-      softmax(0, st, pf);
+    if (active(t0)) {
+      qk(t0, st, false, t0);
+      softmax(t0, st, pf);
     }
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int t = t0; t < n_tiles; ++t) {
       loads(t);
       matrix_phase(t);
       phase_barrier();
-      if (t + 1 < n_act) softmax(t + 1, st, pf);
+      if (active(t + 1)) softmax(t + 1, st, pf);
       wait_all_memory();
       __syncthreads();
     }
   } else {
-    if (n_act > 0) qk(0, st, false, 0);
+    if (active(t0)) qk(t0, st, false, t0);
     __syncthreads();
-    for (int t = 0; t < n_tiles; ++t) {
+    for (int t = t0; t < n_tiles; ++t) {
       loads(t);
-      if (t < n_act) softmax(t, st, pf);
+      if (active(t)) softmax(t, st, pf);
       phase_barrier();
       matrix_phase(t);
       wait_all_memory();
@@ -574,16 +615,22 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + kFwdBM - 1) / kFwdBM;
   const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
   const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
-  if (a.cu_q) {
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, true>), dim3((unsigned)blocks),
+  const Window win{a.window_left, a.window_right};
+  if (a.local) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, true>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-                       a.scale, vl);
+                       a.scale, vl, win);
+  } else if (a.cu_q) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, true, false>), dim3((unsigned)blocks),
+                       dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale, vl, win);
   } else {
-    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, false, false>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
-                       a.scale, vl);
+                       a.scale, vl, win);
   }
   return hipGetLastError();
 }
@@ -595,8 +642,8 @@ int64_t fwd_grid_blocks(int B, int Hq, int Nq) {
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
 #define MI355_FWD_CASE(DTV, DV)                                                 \
   if (a.dtype == DTV && a.d == DV) {                                            \
-    return a.causal ? launch_fwd_t<DTV, DV, true>(a, stream)                    \
-                    : launch_fwd_t<DTV, DV, false>(a, stream);                  \
+    return a.causal && !a.local ? launch_fwd_t<DTV, DV, true>(a, stream)        \
+                                : launch_fwd_t<DTV, DV, false>(a, stream);      \
   }
   MI355_FWD_CASE(kBF16, 128)
   MI355_FWD_CASE(kBF16, 64)

@@ -21,6 +21,11 @@ struct FwdArgs {
   const int* cu_q = nullptr;
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;
+  // Local attention (local = true): key j allowed for row i iff
+  // i + off - window_left <= j <= i + off + window_right, a negative bound
+  // meaning none (off = Nk - Nq); causal is ignored then.
+  bool local = false;
+  int window_left = -1, window_right = -1;
 };
 
 struct SplitArgs {

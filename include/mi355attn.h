@@ -72,6 +72,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_fwd_local — attn_fwd with a local (sliding-window) mask, the "local"
+ * mode that the flash-attention page's kernel traits carry as a flag: key j is
+ * allowed for query row i iff
+ *
+ *   i + (Nk - Nq) - window_left <= j <= i + (Nk - Nq) + window_right
+ *
+ * (aligned to the bottom-right corner, as the causal mask of attn_fwd); a
+ * negative window_left or window_right puts no bound on that side, so (-1, 0)
+ * is attn_fwd's causal mask and (-1, -1) no mask. Only the key tiles a row's
+ * window touches are read. Tensors, head mapping, d, dtype and scale as in
+ * attn_fwd; a row with no allowed key gets O = 0 and LSE = -inf.
+ */
+int attn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int Hq, int Hkv, int Nq, int Nk, int d, float scale, int window_left,
+                   int window_right, int dtype, void* stream);
+
+/*
  * attn_bwd — gradients of attn_fwd: given dout = dL/dO, writes dq, dk, dv, with
  * the probabilities recomputed from the forward's LSE rather than stored (the
  * backward of the flash-attention page's "flash_bwd_kernel" and the llm.c

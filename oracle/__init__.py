@@ -49,6 +49,7 @@ def _load():
         f = ctypes.c_float
         lib.oracle_attn_fwd.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, i64, p, p, i]
+        lib.oracle_attn_fwd_local.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, i, p, p, i]
         lib.oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_attn_bwd.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, p, i]
         lib.oracle_attn_fwd_varlen.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
@@ -59,6 +60,7 @@ def _load():
         lib.oracle_max_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_decode,
                    lib.oracle_decode_paged, lib.oracle_attn_fwd_varlen, lib.oracle_attn_bwd,
+                   lib.oracle_attn_fwd_local,
                    lib.oracle_decode_chunks, lib.oracle_combine, lib.oracle_decode_values,
                    lib.oracle_max_threads):
             fn.restype = ctypes.c_int
@@ -106,6 +108,23 @@ def attn_fwd(q, k, v, dtype: int, scale: float, causal: bool, nthreads: int = 0)
     rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dtype, B, Hq, Hkv, Nq, Nk, d,
                                  float(scale), int(bool(causal)), _ptr(o), _ptr(lse), nthreads)
     _check(rc, "attn_fwd")
+    return o, lse
+
+
+def attn_fwd_local(q, k, v, dtype: int, scale: float, window_left: int, window_right: int,
+                   nthreads: int = 0):
+    """Sliding-window attention (negative bound = none) -> (o [B,Hq,Nq,d], lse [B,Hq,Nq])."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError("shape mismatch")
+    o = np.empty((B, Hq, Nq, d), dtype=np.float64)
+    lse = np.empty((B, Hq, Nq), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_local(_ptr(q), _ptr(k), _ptr(v), dtype, B, Hq, Hkv, Nq, Nk, d,
+                                       float(scale), int(window_left), int(window_right), _ptr(o),
+                                       _ptr(lse), nthreads)
+    _check(rc, "attn_fwd_local")
     return o, lse
 
 

@@ -188,6 +188,47 @@ int oracle_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int
 }
 
 /*
+ * Local (sliding-window) attention forward, the "local" mode flagged in the
+ * flash-attention page's kernel traits: key j is allowed for query row i iff
+ * i + off - window_left <= j <= i + off + window_right with off = Nk - Nq; a
+ * negative bound is no bound on that side. Shapes and outputs as
+ * oracle_attn_fwd. The allowed keys of a row are one contiguous range.
+ */
+int oracle_attn_fwd_local(const uint16_t* q, const uint16_t* k, const uint16_t* v, int dtype,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                          int window_left, int window_right, double* o, double* lse,
+                          int nthreads) {
+    if (check_fwd(B, Hq, Hkv, Nq, Nk, d, dtype)) return -1;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t nrows = (int64_t)B * Hq * Nq;
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* vrow = (double*)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t r = 0; r < nrows; ++r) {
+            const int64_t i = r % Nq, h = (r / Nq) % Hq, b = r / ((int64_t)Nq * Hq);
+            const int64_t g = h * Hkv / Hq;
+            const int64_t centre = i + ((int64_t)Nk - Nq);
+            int64_t lo = window_left < 0 ? 0 : centre - window_left;
+            int64_t hi = window_right < 0 ? Nk : centre + window_right + 1;
+            if (lo < 0) lo = 0;
+            if (hi > Nk) hi = Nk;
+            const uint16_t* kh = k + ((b * Hkv + g) * (int64_t)Nk) * d;
+            const uint16_t* vh = v + ((b * Hkv + g) * (int64_t)Nk) * d;
+            decode_vec(q + r * (int64_t)d, d, dtype, qrow);
+            attend_row(qrow, kh, vh, dtype, lo, hi, d, sc, s, vrow, o + r * (int64_t)d, lse + r);
+        }
+        free(s);
+        free(qrow);
+        free(vrow);
+    }
+    return 0;
+}
+
+/*
  * Attention forward for a chosen set of rows only (for spot checks of large
  * problems). rows holds n triples (b, h, i). o is [n, d], lse is [n].
  */

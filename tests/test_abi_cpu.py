@@ -103,6 +103,20 @@ def test_attn_fwd_varlen_rejects(lib, kw, code):
     assert fwd_varlen(lib, **kw) == code
 
 
+def fwd_local(lib, q=A, k=A, v=A, o=A2, lse=A2, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, d=128, scale=0.1,
+              wl=4, wr=0, dtype=0):
+    return lib.attn_fwd_local(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, wl, wr, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(B=0), -2), (dict(Nk=0), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(Nq=2**23 + 1), -2), (dict(d=48), -3), (dict(dtype=3), -3),
+    (dict(scale=float("nan")), -5), (dict(k=MIS), -4),
+])
+def test_attn_fwd_local_rejects(lib, kw, code):
+    assert fwd_local(lib, **kw) == code
+
+
 def split(lib, q=A, kc=A, vc=A, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2, max_len=64, d=128,
           chunk=16, scale=0.1, dtype=0):
     return lib.attn_decode_split(q, kc, vc, sl, po, pl, B, Hq, Hkv, max_len, d, chunk, scale,

@@ -522,3 +522,36 @@ def test_decode_one_call_full_size_sampled():
                                wl.bits(vc[b:b + 1, :, :L].cpu()), np.array([L], dtype=np.int32),
                                0, w.scale)
         check(o[b:b + 1], lse[b:b + 1], ro, rl, "bf16", "one-call decode seq %d (L=%d)" % (b, L))
+
+
+# --------------------------------------------------------------- local (sliding-window) attention
+
+LOCAL = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype, window_left, window_right
+    (1, 4, 2, 500, 500, 128, "bf16", 63, 0),
+    (1, 4, 2, 500, 500, 128, "bf16", 64, 0),
+    (1, 4, 4, 700, 700, 64, "fp16", 100, 0),
+    (2, 4, 2, 1000, 1000, 128, "bf16", 256, 0),
+    (1, 4, 4, 300, 300, 128, "bf16", 0, 0),
+    (1, 8, 2, 600, 600, 128, "bf16", 128, 128),
+    (1, 4, 4, 257, 513, 128, "bf16", 200, 0),
+    (1, 4, 4, 513, 257, 128, "bf16", 50, 10),
+    (1, 4, 4, 400, 400, 64, "bf16", -1, 0),
+    (1, 4, 4, 400, 400, 128, "bf16", 300, -1),
+    (1, 2, 2, 2048, 2048, 128, "bf16", 512, 0),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,left,right", LOCAL)
+def test_fwd_local(B, Hq, Hkv, Nq, Nk, d, dtype, left, right):
+    seed = zlib.crc32(repr(("local", B, Hq, Hkv, Nq, Nk, d, dtype, left, right)).encode()) % 10000
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed)
+    scale = 1.0 / math.sqrt(d)
+    ob, o = _guarded(q.shape, q.dtype)
+    lb, lse = _guarded((B, Hq, Nq), torch.float32)
+    ea.attn_fwd_local(*_dev(q, k, v), o, lse, left, right, scale)
+    torch.cuda.synchronize()
+    assert _guard_ok(ob, o.numel()) and _guard_ok(lb, lse.numel()), "write outside the outputs"
+    ro, rl = oracle.attn_fwd_local(wl.bits(q), wl.bits(k), wl.bits(v), wl.DTYPE_CODE[dtype], scale,
+                                   left, right)
+    check(o, lse, ro, rl, dtype, "local %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, left, right),))

@@ -562,6 +562,59 @@ def test_backward_closed_form_sums():
             assert np.abs(dk[b, g].sum(axis=0)).max() < 1e-12
 
 
+LOCAL_CASES = [
+    # Nq, Nk, window_left, window_right
+    (13, 13, 3, 0), (13, 13, 0, 0), (13, 13, 4, 2), (9, 15, 5, 0), (15, 9, 2, 1),
+    (11, 11, -1, 3), (11, 11, 2, -1), (10, 10, 100, 0),
+]
+
+
+@pytest.mark.parametrize("Nq,Nk,wl,wr", LOCAL_CASES)
+def test_local_attention_matches_banded_brute_force(Nq, Nk, wl, wr):
+    """Against a numpy brute force with an explicit band mask (no max
+    subtraction), and torch's fp64 SDPA with the same boolean mask."""
+    B, Hq, Hkv, d = 1, 4, 2, 16
+    q = _rand((B, Hq, Nq, d), "bf16", 61)
+    k = _rand((B, Hkv, Nk, d), "bf16", 62)
+    v = _rand((B, Hkv, Nk, d), "bf16", 63)
+    o, lse = oracle.attn_fwd_local(_bits(q), _bits(k), _bits(v), 0, 0.25, wl, wr)
+    i = np.arange(Nq)[:, None] + (Nk - Nq)
+    j = np.arange(Nk)[None, :]
+    band = np.ones((Nq, Nk), dtype=bool)
+    if wl >= 0:
+        band &= j >= i - wl
+    if wr >= 0:
+        band &= j <= i + wr
+    qf, kf, vf = _f64(q), _f64(k), _f64(v)
+    for h in range(Hq):
+        g = h * Hkv // Hq
+        s = 0.25 * qf[0, h] @ kf[0, g].T
+        e = np.where(band, np.exp(s), 0.0)
+        z = e.sum(axis=1)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            ref_o = np.where(z[:, None] > 0, (e / z[:, None]) @ vf[0, g], 0.0)
+            ref_l = np.where(z > 0, np.log(z), -np.inf)
+        assert np.abs(o[0, h] - ref_o).max() < 1e-12
+        assert np.array_equal(np.isneginf(lse[0, h]), np.isneginf(ref_l))
+        fin = np.isfinite(ref_l)
+        assert np.abs(lse[0, h][fin] - ref_l[fin]).max() < 1e-12
+    if band.any(axis=1).all():
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q.double(), k.double().repeat_interleave(2, 1), v.double().repeat_interleave(2, 1),
+            attn_mask=torch.from_numpy(band), scale=0.25)
+        assert np.abs(o - ref.numpy()).max() < 1e-12
+
+
+def test_local_window_limits_reduce_to_causal_and_full():
+    q = _rand((1, 2, 12, 16), "bf16", 71)
+    k = _rand((1, 2, 12, 16), "bf16", 72)
+    v = _rand((1, 2, 12, 16), "bf16", 73)
+    for (wl, wr), causal in (((-1, 0), True), ((-1, -1), False), ((11, 0), True)):
+        o, lse = oracle.attn_fwd_local(_bits(q), _bits(k), _bits(v), 0, 0.25, wl, wr)
+        bo, bl = brute_force(_f64(q), _f64(k), _f64(v), 0.25, causal)
+        assert np.abs(o - bo).max() < 1e-12 and np.abs(lse - bl).max() < 1e-12
+
+
 def test_oracle_rejects_bad_arguments():
     q = np.zeros((1, 3, 4, 8), dtype=np.uint16)
     k = np.zeros((1, 2, 4, 8), dtype=np.uint16)
