@@ -13,6 +13,7 @@ Prints ONE JSON line:
   bwd           the backward (dQ, dK, dV) on the prefill workload, TFLOP/s at 2.5x
                 the forward's flops, timed in a loop of its own
   fwd_local     sliding-window attention (512 keys back) on the prefill shapes
+  fwd_qkvpacked the prefill attention read from one packed [B, N, 3, H, d] tensor
   fwd_varlen    a packed causal prefill batch (8192 tokens in sequences of seeded
                 lengths U[256, 4096]), TFLOP/s, timed in a loop of its own
   decode_auto   the same decode through attn_decode (the library's chunk length)
@@ -56,6 +57,8 @@ def parse():
                     help="skip the backward measurement")
     ap.add_argument("--no-local", action="store_true",
                     help="skip the sliding-window measurement")
+    ap.add_argument("--no-qkv", action="store_true",
+                    help="skip the packed-qkv measurement")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed variable-length prefill measurement")
     ap.add_argument("--no-auto", action="store_true",
@@ -300,6 +303,35 @@ def bench_local(args, torch, np, ea, wp, qg, kg, vg, stream):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
+def bench_qkvpacked(args, torch, np, ea, wp, stream):
+    """The llm_prefill attention read from one packed [B, N, 3, H, d] tensor (no
+    permute) with o written [B, N, H, d]. Timed in a loop of its own."""
+    print("bench: packed qkv input", file=sys.stderr, flush=True)
+    g = torch.Generator(device="cpu").manual_seed(wp.seed + 200)
+    qkv = torch.randn((wp.B, wp.N, 3, wp.Hq, wp.d), generator=g).to(torch.bfloat16).cuda()
+    o = torch.empty((wp.B, wp.N, wp.Hq, wp.d), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((wp.B, wp.Hq, wp.N), dtype=torch.float32, device=qkv.device)
+
+    def run():
+        ea.attn_fwd_qkvpacked(qkv, o, lse, True, wp.scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    tf = 4.0 * wp.B * wp.Hq * wp.N * wp.N * wp.d / 2.0 / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal,token-major>", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def bench_varlen(args, torch, np, ea, wl, dev, stream):
     """A packed causal prefill batch with the llm_prefill token budget (8192 tokens,
     Hq = Hkv = 32, d = 128, bf16) split into sequences of seeded lengths
@@ -501,6 +533,8 @@ def main():
         out["bwd"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream)
     if do_pre and not args.no_local:
         out["fwd_local"] = bench_local(args, torch, np, ea, wp, qg, kg, vg, stream)
+    if do_pre and not args.no_qkv:
+        out["fwd_qkvpacked"] = bench_qkvpacked(args, torch, np, ea, wp, stream)
     if do_pre and not args.no_varlen:
         out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
     if do_dec and not args.no_auto:

@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     attn_decode_workspace,
     attn_fwd,
     attn_fwd_local,
+    attn_fwd_qkvpacked,
     attn_fwd_varlen,
     attn_status_str,
     decode,
@@ -28,6 +29,7 @@ from ._binding import (  # noqa: F401
     default_scale,
     fwd,
     fwd_local,
+    fwd_qkvpacked,
     fwd_varlen,
     load_library,
 )

@@ -27,7 +27,8 @@ ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
 
-EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_bwd", "attn_decode_split",
+EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_fwd_qkvpacked", "attn_bwd",
+           "attn_decode_split",
            "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
            "attn_decode_workspace", "attn_status_str")
 
@@ -54,6 +55,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_local.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, i, p]
+        lib.attn_fwd_qkvpacked.argtypes = [p, p, p, i, i, i, i, f, i, i, p]
         lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         ll = ctypes.c_longlong
         lib.attn_decode.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, f, i, p]
@@ -66,6 +68,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd.restype = i
         lib.attn_fwd_varlen.restype = i
         lib.attn_fwd_local.restype = i
+        lib.attn_fwd_qkvpacked.restype = i
         lib.attn_bwd.restype = i
         lib.attn_decode.restype = i
         lib.attn_decode_workspace.restype = ctypes.c_longlong
@@ -126,6 +129,31 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                                  _stream(stream))
     if st != OK:
         raise AttnError("attn_fwd", st)
+
+
+def attn_fwd_qkvpacked(qkv, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """Calls attn_fwd_qkvpacked. qkv [B,N,3,H,d]; o [B,N,H,d]; lse [B,H,N] fp32."""
+    _gpu(qkv, o, lse)
+    _need(qkv.dim() == 5 and qkv.shape[2] == 3, "qkv must be [B,N,3,H,d]")
+    B, N, _, H, d = qkv.shape
+    _need(o.dtype == qkv.dtype and tuple(o.shape) == (B, N, H, d), "o [B,N,H,d]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N), "lse [B,H,N] fp32")
+    st = load_library().attn_fwd_qkvpacked(_ptr(qkv), _ptr(o), _ptr(lse), B, N, H, d,
+                                           float(scale), int(bool(causal)), _dtype_code(qkv),
+                                           _stream(stream))
+    if st != OK:
+        raise AttnError("attn_fwd_qkvpacked", st)
+
+
+def fwd_qkvpacked(qkv, causal: bool = True, scale: float | None = None, stream=None):
+    """Allocates and returns (o [B,N,H,d], lse [B,H,N]) for a packed qkv tensor."""
+    B, N, _, H, d = qkv.shape
+    if scale is None:
+        scale = default_scale(d)
+    o = torch.empty((B, N, H, d), dtype=qkv.dtype, device=qkv.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=qkv.device)
+    attn_fwd_qkvpacked(qkv, o, lse, causal, scale, stream)
+    return o, lse
 
 
 def attn_fwd_local(q, k, v, o, lse, window_left: int, window_right: int, scale: float,

@@ -39,6 +39,27 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
+extern "C" int attn_fwd_qkvpacked(const void* qkv, void* o, float* lse, int B, int N, int H,
+                                  int d, float scale, int causal, int dtype, void* stream) {
+  if (!qkv || !o || !lse) return MI355ATTN_ERR_NULL_PTR;
+  if (B <= 0 || N <= 0 || H <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (N > kMaxSeq || (int64_t)3 * H * d * 2 * 256 > 0xffffffffLL) return MI355ATTN_ERR_BAD_SHAPE;
+  if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(qkv, 16) || !aligned(o, 16) || !aligned(lse, 4)) return MI355ATTN_ERR_MISALIGNED;
+  if (mi355attn::fwd_grid_blocks(B, H, N) > kMaxGrid || (int64_t)B * H > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  const uint16_t* base = static_cast<const uint16_t*>(qkv);
+  const int64_t hd = (int64_t)H * d;
+  mi355attn::FwdArgs a{base, base + hd, base + 2 * hd, o, lse, B, H, H, N, N, d, scale, causal,
+                       dtype};
+  a.q_stride = a.kv_stride = 3 * H * d;
+  a.o_stride = H * d;
+  a.uniform_len = N;
+  a.total_q = a.total_k = B * N;
+  return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
                               int window_left, int window_right, int dtype, void* stream) {
@@ -99,6 +120,9 @@ extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void
     return MI355ATTN_ERR_BAD_SHAPE;
   mi355attn::FwdArgs a{q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q, max_seqlen_q, d, scale, causal,
                        dtype, cu_seqlens_q, cu_seqlens_k, total_q, total_k};
+  a.q_stride = Hq * d;
+  a.kv_stride = Hkv * d;
+  a.o_stride = Hq * d;
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -130,13 +130,19 @@ __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group
   qtile = causal ? (nqt - 1 - rank) : rank;
 }
 
-// Packed variable-length batches: sequence b owns token rows
-// [cu_q[b], cu_q[b+1]) of q/o [total_q, Hq, d] and [cu_k[b], cu_k[b+1]) of k/v
-// [total_k, Hkv, d]; lse is [Hq, total_q]. Offsets are clamped into the tensors.
+// Token-major batches. With cu_q: packed variable-length sequences, sequence b
+// owns token rows [cu_q[b], cu_q[b+1]) of q / o and [cu_k[b], cu_k[b+1]) of k / v
+// (offsets clamped into the tensors), lse is [Hq, total_q]. Without (uniform_len
+// > 0): sequence b owns rows [b*uniform_len, (b+1)*uniform_len) of all of them,
+// lse is [B, Hq, uniform_len]. Row r of head h of q sits at q + r*q_stride + h*d
+// (k, v: kv_stride; o: o_stride); e.g. a packed [B, N, 3, H, d] qkv tensor is
+// q = qkv, k = qkv + H*d, v = qkv + 2*H*d with q_stride = kv_stride = 3*H*d.
 struct VarLen {
   const int* cu_q;
   const int* cu_k;
   int total_q, total_k;
+  int q_stride, kv_stride, o_stride;
+  int uniform_len;
 };
 
 // Local (sliding-window) attention: key j is allowed for query row i iff
@@ -184,18 +190,23 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
 
   // Row strides (elements) and this sequence's first rows.
   constexpr int QS_DENSE = D;
-  const int QS = VARLEN ? Hq * D : QS_DENSE;   // q / o
-  const int KS = VARLEN ? Hkv * D : QS_DENSE;  // k / v
+  const int QS = VARLEN ? vl.q_stride : QS_DENSE;   // q
+  const int KS = VARLEN ? vl.kv_stride : QS_DENSE;  // k / v
+  const int OS = VARLEN ? vl.o_stride : QS_DENSE;   // o
   int64_t q_row0 = 0, k_row0 = 0;
   if constexpr (VARLEN) {
-    const int qs = min(max(vl.cu_q[b], 0), vl.total_q);
-    const int qe = min(max(vl.cu_q[b + 1], qs), vl.total_q);
-    const int ks = min(max(vl.cu_k[b], 0), vl.total_k);
-    const int ke = min(max(vl.cu_k[b + 1], ks), vl.total_k);
-    q_row0 = qs;
-    k_row0 = ks;
-    Nq = min(qe - qs, Nq);  // rows past the grid's largest length are not computed
-    Nk = ke - ks;
+    if (vl.cu_q) {
+      const int qs = min(max(vl.cu_q[b], 0), vl.total_q);
+      const int qe = min(max(vl.cu_q[b + 1], qs), vl.total_q);
+      const int ks = min(max(vl.cu_k[b], 0), vl.total_k);
+      const int ke = min(max(vl.cu_k[b + 1], ks), vl.total_k);
+      q_row0 = qs;
+      k_row0 = ks;
+      Nq = min(qe - qs, Nq);  // rows past the grid's largest length are not computed
+      Nk = ke - ks;
+    } else {
+      q_row0 = k_row0 = (int64_t)b * vl.uniform_len;
+    }
     if (q0 >= Nq) return;  // the whole workgroup: this sequence is shorter
   }
 
@@ -207,9 +218,9 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int qw0 = q0 + (2 * (wave & 3) + role_b) * 32;  // first query row of this wave
   const int my_row = qw0 + r32;
 
-  const uint16_t* qh = VARLEN ? q + (q_row0 * Hq + h) * D : q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
-  const uint16_t* kh = VARLEN ? k + (k_row0 * Hkv + g) * D : k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
-  const uint16_t* vh = VARLEN ? v + (k_row0 * Hkv + g) * D : v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  const uint16_t* qh = VARLEN ? q + q_row0 * QS + (int64_t)h * D : q + ((int64_t)b * Hq + h) * (int64_t)Nq * D;
+  const uint16_t* kh = VARLEN ? k + k_row0 * KS + (int64_t)g * D : k + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  const uint16_t* vh = VARLEN ? v + k_row0 * KS + (int64_t)g * D : v + ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
   // Q rows of this workgroup. Dense: the head's rows, addressed from row 0.
   // Packed: based at row q0, ranging over the rows below Nq (strided rows).
   const int q_rows = min(kFwdBM, Nq - q0);
@@ -591,7 +602,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     }
   }
   wait_lgkmcnt0();
-  uint16_t* otile = VARLEN ? o + ((q_row0 + qw0) * Hq + h) * D
+  uint16_t* otile = VARLEN ? o + (q_row0 + qw0) * OS + (int64_t)h * D
                            : o + (((int64_t)b * Hq + h) * (int64_t)Nq + qw0) * D;
   const int cl = lane % CPR, rl = lane / CPR;
 #pragma unroll
@@ -599,12 +610,16 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const int r = s0 + rl;
     const u32x4_t val = *reinterpret_cast<const u32x4_t*>(qslot + r * ROW + ((cl ^ (r & (CPR - 1))) << 4));
     if (qw0 + r < Nq)
-      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(otile + (int64_t)r * QS + cl * 8));
+      __builtin_nontemporal_store(val, reinterpret_cast<u32x4_t*>(otile + (int64_t)r * OS + cl * 8));
   }
   if (my_row < Nq && half == 0) {
     const float out = empty ? -INFINITY : kLn2 * (m_used + fast_log2(l_row));
-    if constexpr (VARLEN)
-      lse[(int64_t)h * vl.total_q + q_row0 + my_row] = out;
+    if constexpr (VARLEN) {
+      if (vl.cu_q)
+        lse[(int64_t)h * vl.total_q + q_row0 + my_row] = out;
+      else
+        lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
+    }
     else
       lse[((int64_t)b * Hq + h) * (int64_t)Nq + my_row] = out;
   }
@@ -614,14 +629,15 @@ template <int DT, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + kFwdBM - 1) / kFwdBM;
   const int64_t blocks = (int64_t)a.B * a.Hq * nqt;
-  const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k};
+  const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_stride, a.kv_stride, a.o_stride,
+                  a.uniform_len};
   const Window win{a.window_left, a.window_right};
   if (a.local) {
     hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, true>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
                        a.scale, vl, win);
-  } else if (a.cu_q) {
+  } else if (a.cu_q || a.uniform_len > 0) {
     hipLaunchKernelGGL((attn_fwd_kernel<DT, D, CAUSAL, true, false>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,

@@ -21,6 +21,10 @@ struct FwdArgs {
   const int* cu_q = nullptr;
   const int* cu_k = nullptr;
   int total_q = 0, total_k = 0;
+  // Token-major layouts (cu_q set, or uniform_len > 0): row strides in
+  // elements of q, of k / v and of o, row r of head h at base + r*stride + h*d.
+  int q_stride = 0, kv_stride = 0, o_stride = 0;
+  int uniform_len = 0;
   // Local attention (local = true): key j allowed for row i iff
   // i + off - window_left <= j <= i + off + window_right, a negative bound
   // meaning none (off = Nk - Nq); causal is ignored then.

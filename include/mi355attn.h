@@ -72,6 +72,22 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
              int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_fwd_qkvpacked — attn_fwd reading q, k and v straight out of one packed
+ * projection output, with no permute (the llm.c page's attention_forward first
+ * permutes a [B, N, 3, H, d] qkv tensor into separate q, k, v; here the kernel
+ * addresses the packed rows directly), and writing o token-major, ready for the
+ * output projection:
+ *
+ *   qkv [B, N, 3, H, d]  dtype  (read: q = qkv[:, :, 0], k = [:, :, 1], v = [:, :, 2])
+ *   o   [B, N, H, d]     dtype  (written, rounded to nearest even)
+ *   lse [B, H, N]        float  (written)
+ *
+ * Hq = Hkv = H; causal, d, dtype and scale as in attn_fwd.
+ */
+int attn_fwd_qkvpacked(const void* qkv, void* o, float* lse, int B, int N, int H, int d,
+                       float scale, int causal, int dtype, void* stream);
+
+/*
  * attn_fwd_local — attn_fwd with a local (sliding-window) mask, the "local"
  * mode that the flash-attention page's kernel traits carry as a flag: key j is
  * allowed for query row i iff

@@ -50,6 +50,7 @@ def _load():
         lib.oracle_attn_fwd.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_attn_fwd_rows.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, p, i64, p, p, i]
         lib.oracle_attn_fwd_local.argtypes = [p, p, p, i, i, i, i, i, i, i, f, i, i, p, p, i]
+        lib.oracle_attn_fwd_qkvpacked.argtypes = [p, i, i, i, i, i, f, i, p, p, i]
         lib.oracle_decode.argtypes = [p, p, p, p, i, i, i, i, i, i, f, p, p, i]
         lib.oracle_attn_bwd.argtypes = [p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, p, i]
         lib.oracle_attn_fwd_varlen.argtypes = [p, p, p, p, p, i, i, i, i, i, i, i, f, i, p, p, i]
@@ -60,7 +61,7 @@ def _load():
         lib.oracle_max_threads.argtypes = []
         for fn in (lib.oracle_attn_fwd, lib.oracle_attn_fwd_rows, lib.oracle_decode,
                    lib.oracle_decode_paged, lib.oracle_attn_fwd_varlen, lib.oracle_attn_bwd,
-                   lib.oracle_attn_fwd_local,
+                   lib.oracle_attn_fwd_local, lib.oracle_attn_fwd_qkvpacked,
                    lib.oracle_decode_chunks, lib.oracle_combine, lib.oracle_decode_values,
                    lib.oracle_max_threads):
             fn.restype = ctypes.c_int
@@ -108,6 +109,20 @@ def attn_fwd(q, k, v, dtype: int, scale: float, causal: bool, nthreads: int = 0)
     rc = _load().oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), dtype, B, Hq, Hkv, Nq, Nk, d,
                                  float(scale), int(bool(causal)), _ptr(o), _ptr(lse), nthreads)
     _check(rc, "attn_fwd")
+    return o, lse
+
+
+def attn_fwd_qkvpacked(qkv, dtype: int, scale: float, causal: bool, nthreads: int = 0):
+    """Attention from a packed qkv [B,N,3,H,d] -> (o [B,N,H,d], lse [B,H,N])."""
+    qkv = _u16(qkv)
+    if qkv.ndim != 5 or qkv.shape[2] != 3:
+        raise ValueError("qkv must be [B,N,3,H,d]")
+    B, N, _, H, d = qkv.shape
+    o = np.empty((B, N, H, d), dtype=np.float64)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _load().oracle_attn_fwd_qkvpacked(_ptr(qkv), dtype, B, N, H, d, float(scale),
+                                           int(bool(causal)), _ptr(o), _ptr(lse), nthreads)
+    _check(rc, "attn_fwd_qkvpacked")
     return o, lse
 
 

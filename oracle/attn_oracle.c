@@ -229,6 +229,51 @@ int oracle_attn_fwd_local(const uint16_t* q, const uint16_t* k, const uint16_t* 
 }
 
 /*
+ * Attention forward from a packed projection output qkv [B, N, 3, H, d] (the
+ * layout the llm.c page's attention_forward permutes apart before its matrix
+ * products): q, k and v of head h and token n are qkv[b][n][0|1|2][h]. Output
+ * o [B, N, H, d] (token-major) and lse [B, H, N]. Each (b, h) gathers its
+ * three row sets into contiguous scratch and attends as oracle_attn_fwd.
+ */
+int oracle_attn_fwd_qkvpacked(const uint16_t* qkv, int dtype, int B, int N, int H, int d,
+                              float scale, int causal, double* o, double* lse, int nthreads) {
+    if (check_fwd(B, H, H, N, N, d, dtype)) return -1;
+    set_threads(nthreads);
+    const double sc = (double)scale;
+    const int64_t units = (int64_t)B * H;
+    const int64_t tok = (int64_t)3 * H * d;  /* elements per token */
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+        double* qrow = (double*)malloc(sizeof(double) * (size_t)d);
+        double* vrow = (double*)malloc(sizeof(double) * (size_t)d);
+        uint16_t* kg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * (size_t)d);
+        uint16_t* vg = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)N * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < units; ++u) {
+            const int64_t b = u / H, h = u % H;
+            const uint16_t* base = qkv + b * (int64_t)N * tok;
+            for (int64_t j = 0; j < N; ++j) {
+                memcpy(kg + j * d, base + j * tok + (H + h) * (int64_t)d, sizeof(uint16_t) * (size_t)d);
+                memcpy(vg + j * d, base + j * tok + (2 * H + h) * (int64_t)d,
+                       sizeof(uint16_t) * (size_t)d);
+            }
+            for (int64_t i = 0; i < N; ++i) {
+                decode_vec(base + i * tok + h * (int64_t)d, d, dtype, qrow);
+                attend_row(qrow, kg, vg, dtype, 0, causal_end(i, N, N, causal), d, sc, s, vrow,
+                           o + ((b * N + i) * H + h) * (int64_t)d, lse + (b * H + h) * (int64_t)N + i);
+            }
+        }
+        free(s);
+        free(qrow);
+        free(vrow);
+        free(kg);
+        free(vg);
+    }
+    return 0;
+}
+
+/*
  * Attention forward for a chosen set of rows only (for spot checks of large
  * problems). rows holds n triples (b, h, i). o is [n, d], lse is [n].
  */

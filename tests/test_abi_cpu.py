@@ -117,6 +117,19 @@ def test_attn_fwd_local_rejects(lib, kw, code):
     assert fwd_local(lib, **kw) == code
 
 
+def qkvp(lib, qkv=A, o=A2, lse=A2, B=2, N=64, H=4, d=128, scale=0.1, causal=1, dtype=0):
+    return lib.attn_fwd_qkvpacked(qkv, o, lse, B, N, H, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(qkv=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(B=0), -2), (dict(N=0), -2),
+    (dict(H=0), -2), (dict(N=2**23 + 1), -2), (dict(d=32), -3), (dict(dtype=4), -3),
+    (dict(scale=-1.0), -5), (dict(causal=7), -5), (dict(qkv=MIS), -4),
+])
+def test_attn_fwd_qkvpacked_rejects(lib, kw, code):
+    assert qkvp(lib, **kw) == code
+
+
 def split(lib, q=A, kc=A, vc=A, sl=A2, po=A2, pl=A2, B=2, Hq=8, Hkv=2, max_len=64, d=128,
           chunk=16, scale=0.1, dtype=0):
     return lib.attn_decode_split(q, kc, vc, sl, po, pl, B, Hq, Hkv, max_len, d, chunk, scale,

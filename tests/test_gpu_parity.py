@@ -555,3 +555,35 @@ def test_fwd_local(B, Hq, Hkv, Nq, Nk, d, dtype, left, right):
     ro, rl = oracle.attn_fwd_local(wl.bits(q), wl.bits(k), wl.bits(v), wl.DTYPE_CODE[dtype], scale,
                                    left, right)
     check(o, lse, ro, rl, dtype, "local %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, left, right),))
+
+
+# --------------------------------------------------------------- packed qkv input
+
+QKV = [
+    # B, N, H, d, dtype, causal
+    (2, 300, 4, 128, "bf16", True),
+    (1, 129, 2, 64, "fp16", False),
+    (1, 1000, 8, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,N,H,d,dtype,causal", QKV)
+def test_fwd_qkvpacked(B, N, H, d, dtype, causal):
+    seed = zlib.crc32(repr(("qkv", B, N, H, d, dtype, causal)).encode()) % 10000
+    g = torch.Generator().manual_seed(seed)
+    qkv = torch.randn((B, N, 3, H, d), generator=g).to(wl.DTYPES[dtype])
+    scale = 1.0 / math.sqrt(d)
+    ob, o = _guarded((B, N, H, d), qkv.dtype)
+    lb, lse = _guarded((B, H, N), torch.float32)
+    qkvd = qkv.cuda()
+    ea.attn_fwd_qkvpacked(qkvd, o, lse, causal, scale)
+    torch.cuda.synchronize()
+    assert _guard_ok(ob, o.numel()) and _guard_ok(lb, lse.numel()), "write outside the outputs"
+    ro, rl = oracle.attn_fwd_qkvpacked(wl.bits(qkv), wl.DTYPE_CODE[dtype], scale, causal)
+    check(o, lse, ro, rl, dtype, "qkvpacked %s" % ((B, N, H, d, dtype, causal),))
+    # same tiles and arithmetic as the dense kernel on the unpacked tensors
+    q, k, v = (qkvd[:, :, i].transpose(1, 2).contiguous() for i in range(3))
+    od, ld = ea.fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(od.transpose(1, 2).contiguous().view(torch.int16), o.view(torch.int16))
+    assert torch.equal(ld, lse)

@@ -615,6 +615,18 @@ def test_local_window_limits_reduce_to_causal_and_full():
         assert np.abs(o - bo).max() < 1e-12 and np.abs(lse - bl).max() < 1e-12
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_qkvpacked_equals_attention_of_the_unpacked_tensors(causal):
+    """Unpacking is a pure permutation (done here by torch indexing): the packed
+    oracle must equal the dense oracle on q, k, v taken out of qkv."""
+    B, N, H, d = 2, 19, 3, 16
+    qkv = _rand((B, N, 3, H, d), "bf16", 81)
+    o, lse = oracle.attn_fwd_qkvpacked(_bits(qkv), 0, 0.25, causal)
+    q, k, v = (qkv[:, :, i].transpose(1, 2).contiguous() for i in range(3))
+    ro, rl = oracle.attn_fwd(_bits(q), _bits(k), _bits(v), 0, 0.25, causal)
+    assert np.array_equal(o, ro.transpose(0, 2, 1, 3)) and np.array_equal(lse, rl)
+
+
 def test_oracle_rejects_bad_arguments():
     q = np.zeros((1, 3, 4, 8), dtype=np.uint16)
     k = np.zeros((1, 2, 4, 8), dtype=np.uint16)
