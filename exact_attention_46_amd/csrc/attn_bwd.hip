@@ -15,15 +15,19 @@
 //  * attn_bwd_dkdv_kernel: one workgroup per (batch, kv-head, 128 keys); each of
 //    its 4 waves owns 32 keys, whose K and V rows it keeps in registers as the
 //    B operands of S = Q K^T and dP = dO V^T (32x32x16 MFMA, fp32 accumulate).
-//    It walks 32-row tiles of Q and dO (every query head of the group) staged in
-//    LDS. The S / dP accumulators hold one key per lane and 16 rows per lane,
+//    It walks 64-row tiles of Q and dO (every query head of the group) staged in
+//    LDS with their LSE and D, two buffers deep: the next tile's loads go out
+//    right after the barrier that publishes the current one and land while the
+//    current one is computed. The S / dP accumulators hold one key per lane and
+//    16 rows per lane,
 //    which is the B-operand layout of the next products, so P and dS enter
 //    dV^T += dO^T P and dK^T += Q^T dS as they are (rounded to the input dtype),
 //    with dO^T and Q^T read from the staged tiles by transposing LDS reads.
 //  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (batch, head);
 //    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
-//    of K and V staged in LDS: S^T = K Q^T, dP^T = V dO^T (one query row per
-//    lane), dS^T, then dQ^T += K^T dS^T with K^T from transposing reads.
+//    of K and V staged in LDS (two buffers deep, as above): S^T = K Q^T,
+//    dP^T = V dO^T (one query row per lane), dS^T, then dQ^T += K^T dS^T with
+//    K^T from transposing reads.
 // The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
 // instead of 5), which is what removes the atomics on dQ.
 #include "common.hpp"
@@ -35,7 +39,7 @@ constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kBwdKeysWG = 32 * kBwdWaves;  // keys per dK/dV workgroup
 constexpr int kBwdRowsWG = 32 * kBwdWaves;  // query rows per dQ workgroup
-constexpr int kBwdQT = 32;                  // query rows per dK/dV step
+constexpr int kBwdQT = 64;                  // query rows per dK/dV step
 constexpr int kBwdKT = 64;                  // keys per dQ step
 
 // LDS tiles are row-major with the 16-byte chunk index XOR-swizzled by the low
@@ -67,6 +71,15 @@ __device__ __forceinline__ void stage_rows(const uint16_t* base, int r0, int n, 
   }
 }
 
+// Stages 64 consecutive floats src[r0 .. r0+63] (entries at or past n read as
+// zero) into LDS with one 4-byte-per-lane load of the calling wave.
+__device__ __forceinline__ void stage_floats64(const float* src, int r0, int n, float* dst,
+                                               int lane) {
+  const auto rs = make_rsrc(src + r0, (uint32_t)max(0, n - r0) * 4u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4,
+                                           (uint32_t)lane * 4u, 0, 0, 0);
+}
+
 // A-operand row read of a staged tile: row r, logical 16-byte chunk c.
 template <int D>
 __device__ __forceinline__ u32x4_t tile_row16(const unsigned char* tile, int r, int c) {
@@ -87,7 +100,8 @@ __device__ __forceinline__ u32x4_t tile_tr(const unsigned char* tile, int ks, in
   const int r1 = 16 * ks + 4 * half + kk, r2 = r1 + 8;
   const unsigned char* p1 = tile + r1 * ROW + (((col >> 3) ^ bwd_swz<D>(r1)) << 4) + (col & 7) * 2;
   const unsigned char* p2 = tile + r2 * ROW + (((col >> 3) ^ bwd_swz<D>(r2)) << 4) + (col & 7) * 2;
-  const u32x2_t lo = lds_read_tr16(p1), hi = lds_read_tr16(p2);
+  const u32x2_t lo = lds_read_tr16_staged((const lds_s16x4_t*)p1);
+  const u32x2_t hi = lds_read_tr16_staged((const lds_s16x4_t*)p2);
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -142,9 +156,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      int Nq, int Nk, float scale) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdQT * ROW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILE];
-  unsigned char* tq = smem;
-  unsigned char* tdo = smem + TILE;
+  constexpr int STAGE = 2 * TILE + 2 * kBwdQT * 4;  // Q, dO, LSE, D
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -182,47 +195,64 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   }
   const float c = scale * kLog2e;
 
-  // Query rows that may see any key of this workgroup: i >= k0 - off.
+  // Steps: every query head of the group, its 64-row tiles from the first one
+  // whose rows may see a key of this workgroup (i >= k0 - off when causal).
   const int r_begin = CAUSAL ? max(0, k0 - off) : 0;
   const int t_begin = r_begin / kBwdQT;
   const int t_end = (Nq + kBwdQT - 1) / kBwdQT;
-  for (int hh = 0; hh < group; ++hh) {
-    const int h = g * group + hh;
-    const int64_t qoff = ((int64_t)b * Hq + h) * (int64_t)Nq;  // row index of (b, h, 0)
-    for (int t = t_begin; t < t_end; ++t) {
-      const int r0 = t * kBwdQT;
-      __syncthreads();  // the previous tile's reads are done
-      stage_rows<D, kBwdQT>(q + qoff * D, r0, Nq, tq, tid);
-      stage_rows<D, kBwdQT>(dout + qoff * D, r0, Nq, tdo, tid);
-      // This lane's rows: r0 + 8*(e/4) + 4*half + e%4 -> LSE (log2 units) and D.
-      float l2[16], dl[16];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int row = r0 + 8 * gq + 4 * half + x;
-          const bool ok = row < Nq;
-          l2[4 * gq + x] = ok ? lse[qoff + row] * kLog2e : 0.f;
-          dl[4 * gq + x] = ok ? delta[qoff + row] : 0.f;
-        }
-      }
-      wait_all_memory();
-      __syncthreads();
+  const int per_head = max(0, t_end - t_begin);
+  const int n_steps = group * per_head;
+  // Stage loads of step i into buffer i & 1: Q and dO rows (all waves), LSE
+  // (wave 0) and D (wave 1).
+  auto issue = [&](int i) {
+    const int h = g * group + i / per_head;
+    const int r0 = (t_begin + i % per_head) * kBwdQT;
+    const int64_t qoff = ((int64_t)b * Hq + h) * (int64_t)Nq;
+    unsigned char* st = smem + (i & 1) * STAGE;
+    stage_rows<D, kBwdQT>(q + qoff * D, r0, Nq, st, tid);
+    stage_rows<D, kBwdQT>(dout + qoff * D, r0, Nq, st + TILE, tid);
+    if (wave == 0) stage_floats64(lse + qoff, r0, Nq, (float*)(st + 2 * TILE), lane);
+    if (wave == 1) stage_floats64(delta + qoff, r0, Nq, (float*)(st + 2 * TILE) + kBwdQT, lane);
+  };
+  if (n_steps > 0) issue(0);
+  for (int i = 0; i < n_steps; ++i) {
+    const int r0 = (t_begin + i % per_head) * kBwdQT;
+    // Step i's loads (this wave's) have landed; the barrier publishes every
+    // wave's and also ends all reads of step i-1, whose buffer the loads of
+    // step i+1 reuse.
+    wait_all_memory();
+    __syncthreads();
+    if (i + 1 < n_steps) issue(i + 1);
+    const unsigned char* st = smem + (i & 1) * STAGE;
+    const unsigned char* tq = st;
+    const unsigned char* tdo = st + TILE;
+    const float* slse = (const float*)(st + 2 * TILE);
+    const float* sdl = slse + kBwdQT;
 
+#pragma unroll
+    for (int rb = 0; rb < kBwdQT / 32; ++rb) {
       // S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys.
       f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        s = mfma32x32x16<DT>(tile_row16<D>(tq, r32, half * DS + ds), kf[ds], s);
-        dp = mfma32x32x16<DT>(tile_row16<D>(tdo, r32, half * DS + ds), vf[ds], dp);
+        s = mfma32x32x16<DT>(tile_row16<D>(tq, 32 * rb + r32, half * DS + ds), kf[ds], s);
+        dp = mfma32x32x16<DT>(tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds), vf[ds], dp);
       }
       float p[16], dsv[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = r0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
-        p[e] = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l2[e])) : 0.f;
-        dsv[e] = p[e] * (dp[e] - dl[e]);
+      for (int gq = 0; gq < 4; ++gq) {
+        // this lane's rows 32rb + 8gq + 4half + 0..3: LSE and D from LDS
+        const int lr = 32 * rb + 8 * gq + 4 * half;
+        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + lr);
+        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(sdl + lr);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const int e = 4 * gq + x;
+          const int row = r0 + lr + x;
+          const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
+          p[e] = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l4[x] * kLog2e)) : 0.f;
+          dsv[e] = p[e] * (dp[e] - d4[x]);
+        }
       }
       u32x4_t pf[2], sf[2];
 #pragma unroll
@@ -234,13 +264,13 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                            pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
                            pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (d x keys).
+      // dV^T += dO^T P, dK^T += Q^T dS (d x keys) over these 32 rows.
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dva[db] = mfma32x32x16<DT>(tile_tr<D>(tdo, ks, db, lane), pf[ks], dva[db]);
-          dka[db] = mfma32x32x16<DT>(tile_tr<D>(tq, ks, db, lane), sf[ks], dka[db]);
+          dva[db] = mfma32x32x16<DT>(tile_tr<D>(tdo, 2 * rb + ks, db, lane), pf[ks], dva[db]);
+          dka[db] = mfma32x32x16<DT>(tile_tr<D>(tq, 2 * rb + ks, db, lane), sf[ks], dka[db]);
         }
     }
   }
@@ -274,9 +304,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdKT * ROW;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * TILE];
-  unsigned char* tk = smem;
-  unsigned char* tv = smem + TILE;
+  constexpr int STAGE = 2 * TILE;  // K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -318,13 +347,21 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   int kv_end = Nk;
   if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kBwdRowsWG, Nq) - 1 + off + 1));
   const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t & 1) * STAGE;
+    stage_rows<D, kBwdKT>(k + kvoff, t * kBwdKT, Nk, st, tid);
+    stage_rows<D, kBwdKT>(v + kvoff, t * kBwdKT, Nk, st + TILE, tid);
+  };
+  if (n_tiles > 0) issue(0);
   for (int t = 0; t < n_tiles; ++t) {
     const int k0 = t * kBwdKT;
-    __syncthreads();
-    stage_rows<D, kBwdKT>(k + kvoff, k0, Nk, tk, tid);
-    stage_rows<D, kBwdKT>(v + kvoff, k0, Nk, tv, tid);
+    // Tile t has landed (this wave's loads; the barrier publishes the rest and
+    // ends all reads of tile t-1, whose buffer tile t+1 reuses).
     wait_all_memory();
     __syncthreads();
+    if (t + 1 < n_tiles) issue(t + 1);
+    const unsigned char* tk = smem + (t & 1) * STAGE;
+    const unsigned char* tv = tk + TILE;
 
     // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
     f32x16_t s[2], dp[2];
