@@ -128,9 +128,9 @@ def record_traffic(fetch_dir, write_dir):
                             "write_counter_bytes_per_byte": round(w_cal, 4)}}
     for name, match in (("attn_fwd_kernel/llm_prefill", "attn_fwd_kernel"),
                         ("attn_decode_split_kernel/decode",
-                         "attn_decode_split_kernel<0, 128, false>"),
+                         "attn_decode_split_kernel<0, 128, false, false>"),
                         ("attn_decode_split_kernel/decode_paged",
-                         "attn_decode_split_kernel<0, 128, true>")):
+                         "attn_decode_split_kernel<0, 128, true, false>")):
         fb = pick(fetch, match) * 1024.0 / f_cal
         wb = pick(write, match) * 1024.0 / w_cal
         rec[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
