@@ -42,12 +42,18 @@ constexpr int kBwdRowsWG = 32 * kBwdWaves;  // query rows per dQ workgroup
 constexpr int kBwdQT = 64;                  // query rows per dK/dV step
 constexpr int kBwdKT = 64;                  // keys per dQ step
 
-// LDS tiles are row-major with the 16-byte chunk index XOR-swizzled by the low
-// bits of the row (as the forward's K tile), read both as rows (16-byte reads)
-// and transposed (ds_read_b64_tr_b16).
+// LDS tiles are row-major with the 16-byte chunk index XOR-swizzled by a
+// function of the row, and each is read both as rows (16-byte reads of one
+// logical chunk from 16 consecutive rows: the swizzle must be a bijection on
+// any 16 consecutive rows) and transposed (each 32-lane half of a
+// ds_read_b64_tr_b16 covers 4 chunks c0..c0+3 of an aligned group of 4 rows:
+// within such a group the swizzle's low two bits must be constant and its high
+// two bits distinct). At d = 128, 4 (r & 3) + ((r >> 2) & 3) meets both (the
+// row-only swizzle r & 15 of the forward's K tile cost the backward 5e7 bank
+// conflict cycles per dK/dV launch on llm_prefill).
 template <int D>
 __device__ __forceinline__ int bwd_swz(int row) {
-  return D == 128 ? (row & 15) : ((row >> 1) & 7);
+  return D == 128 ? 4 * (row & 3) + ((row >> 2) & 3) : ((row >> 1) & 7);
 }
 
 // Stages rows [r0, r0 + ROWS) of a [*, D] row-major tensor (rows >= n read as
@@ -231,12 +237,30 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 #pragma unroll
     for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+      // Operands are read as whole batches ahead of their MFMA chains (one LDS
+      // latency per batch instead of one per product): the row operands of S
+      // and dP, then the transposed operands of dV and dK, whose latency hides
+      // behind the S / dP products and the element-wise work.
+      u32x4_t qa[DS], da[DS], ta[2 * DB], tb[2 * DB];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        qa[ds] = tile_row16<D>(tq, 32 * rb + r32, half * DS + ds);
+        da[ds] = tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          ta[ks * DB + db] = tile_tr<D>(tdo, 2 * rb + ks, db, lane);
+          tb[ks * DB + db] = tile_tr<D>(tq, 2 * rb + ks, db, lane);
+        }
+      __builtin_amdgcn_sched_barrier(0);
       // S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys.
       f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        s = mfma32x32x16<DT>(tile_row16<D>(tq, 32 * rb + r32, half * DS + ds), kf[ds], s);
-        dp = mfma32x32x16<DT>(tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds), vf[ds], dp);
+        s = mfma32x32x16<DT>(qa[ds], kf[ds], s);
+        dp = mfma32x32x16<DT>(da[ds], vf[ds], dp);
       }
       float p[16], dsv[16];
 #pragma unroll
@@ -269,9 +293,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          dva[db] = mfma32x32x16<DT>(tile_tr<D>(tdo, 2 * rb + ks, db, lane), pf[ks], dva[db]);
-          dka[db] = mfma32x32x16<DT>(tile_tr<D>(tq, 2 * rb + ks, db, lane), sf[ks], dka[db]);
+          dva[db] = mfma32x32x16<DT>(ta[ks * DB + db], pf[ks], dva[db]);
+          dka[db] = mfma32x32x16<DT>(tb[ks * DB + db], sf[ks], dka[db]);
         }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -364,15 +389,32 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const unsigned char* tv = tk + TILE;
 
     // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
+    // Operands are read as batches ahead of their MFMA chains: K and V rows of
+    // a key block, then the K^T operands of dQ, whose latency hides behind the
+    // products and the element-wise work.
     f32x16_t s[2], dp[2];
+    u32x4_t ta[4 * DB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      u32x4_t ka[DS], va[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        ka[ds] = tile_row16<D>(tk, 32 * kb + r32, half * DS + ds);
+        va[ds] = tile_row16<D>(tv, 32 * kb + r32, half * DS + ds);
+      }
+      if (kb == 1) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) ta[ks * DB + db] = tile_tr<D>(tk, ks, db, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
       s[kb] = (f32x16_t){};
       dp[kb] = (f32x16_t){};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        s[kb] = mfma32x32x16<DT>(tile_row16<D>(tk, 32 * kb + r32, half * DS + ds), qf[ds], s[kb]);
-        dp[kb] = mfma32x32x16<DT>(tile_row16<D>(tv, 32 * kb + r32, half * DS + ds), dof[ds], dp[kb]);
+        s[kb] = mfma32x32x16<DT>(ka[ds], qf[ds], s[kb]);
+        dp[kb] = mfma32x32x16<DT>(va[ds], dof[ds], dp[kb]);
       }
     }
     // dS^T, packed as the B operand of dQ^T += K^T dS^T (4 steps of 16 keys).
@@ -395,8 +437,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sf[ks], dqa[db]);
+      for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(ta[ks * DB + db], sf[ks], dqa[db]);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // dQ = scale * (dQ^T)^T: lane row r32, d = 32db + 8(e/4) + 4half + e%4.
