@@ -244,14 +244,20 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if constexpr (PAGED) {
       // Load i covers logical rows r0 + i*RPL .. +RPL-1, all inside one page
       // (RPL divides the page size). Rows at or past L, and pages outside
-      // [0, num_pages), read as zeros.
+      // [0, num_pages), read as zeros. The tile's 32 rows span at most two
+      // pages (page size >= 16), whose physical numbers are looked up once.
+      const int lp_a = r0 / pk.page_size, lp_b = (r0 + kSplitBN - 1) / pk.page_size;
+      int phys_a = p.pg[0], phys_b = p.pg[0];
+#pragma unroll
+      for (int k = 1; k < kMaxItemPages; ++k) {
+        phys_a = (lp_a - p.lp0 == k) ? p.pg[k] : phys_a;
+        phys_b = (lp_b - p.lp0 == k) ? p.pg[k] : phys_b;
+      }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int ri = r0 + i * Lay::kRowsPerLoad;
         const int lp = ri / pk.page_size;
-        int phys = p.pg[0];
-#pragma unroll
-        for (int k = 1; k < kMaxItemPages; ++k) phys = (lp - p.lp0 == k) ? p.pg[k] : phys;
+        const int phys = lp == lp_a ? phys_a : phys_b;
         int rows = min(p.L - ri, Lay::kRowsPerLoad);
         if (phys < 0 || phys >= pk.num_pages) rows = 0;
         if (rows < 0) rows = 0;
