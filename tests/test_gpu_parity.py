@@ -415,7 +415,7 @@ def test_fwd_varlen_full_size_sampled():
 
 # --------------------------------------------------------------- backward
 
-# Gradient tolerance. There is no gate for gradients in the task; the errors
+# Gradient tolerance. No gate is set for gradients elsewhere; the errors
 # come from rounding P and dS to the input dtype before their products (relative
 # 2^-9 for bf16, 2^-12 for fp16 per term) and from rounding the outputs, so the
 # gate is relative to the largest reference gradient of the tensor: bf16 2^-6,
