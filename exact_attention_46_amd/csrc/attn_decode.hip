@@ -39,6 +39,8 @@
 // rescaling combine of the aprender-gpu "flash_decoding/reduce_kernel.rs" page
 // (global max of the chunk LSEs, weights exp(LSE_c - M), normalised weighted
 // sum), skipping chunks whose LSE is -inf.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -571,18 +573,19 @@ int64_t split_work_items(int B, int Hkv, int max_len, int chunk) {
 }
 
 static int device_cus() {
-  // Queried once per device (the value never changes).
-  static int cached[64] = {0};
+  // Queried once per device (the value never changes); the cache is atomic so
+  // concurrent first calls from several host threads are well defined.
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 // Chunk length for attn_decode: enough work items (about eight per resident

@@ -5,8 +5,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Tensors are dense, row-major, in device memory owned by the caller. The
- *    library allocates nothing, keeps no workspace and no mutable global state,
- *    and may be called from several host threads at once.
+ *    library allocates nothing, keeps no workspace and no mutable global state
+ *    (apart from a per-device cache of the compute-unit count, which the split
+ *    kernels size their grid by), and may be called from several host threads
+ *    at once.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *    Every call only enqueues work on that stream and returns at once.
  *  - The return value covers argument checks and the launch itself
