@@ -12,22 +12,31 @@
 //
 // Three kernels on one stream, no atomics (the result is deterministic):
 //  * attn_bwd_delta_kernel: D for every query row.
-//  * attn_bwd_dkdv_kernel: one workgroup per (batch, kv-head, 128 keys); each of
-//    its 4 waves owns 32 keys, whose K and V rows it keeps in registers as the
-//    B operands of S = Q K^T and dP = dO V^T (32x32x16 MFMA, fp32 accumulate).
-//    It walks 64-row tiles of Q and dO (every query head of the group) staged in
-//    LDS with their LSE and D, two buffers deep: the next tile's loads go out
-//    right after the barrier that publishes the current one and land while the
-//    current one is computed. The S / dP accumulators hold one key per lane and
-//    16 rows per lane,
-//    which is the B-operand layout of the next products, so P and dS enter
-//    dV^T += dO^T P and dK^T += Q^T dS as they are (rounded to the input dtype),
-//    with dO^T and Q^T read from the staged tiles by transposing LDS reads.
+//  * attn_bwd_dkdv_kernel: one workgroup of 8 waves per (batch, kv-head, 128
+//    keys). Two waves own each 32 keys: the first keeps their K rows in
+//    registers, computes S = Q K^T and P and accumulates dV^T += dO^T P; the
+//    second keeps their V rows, computes dP = dO V^T, takes P from the first
+//    through LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS (32x32x16
+//    MFMA, fp32 accumulate). Each wave holds one operand block and one
+//    accumulator, so it fits in 256 registers and two waves share each SIMD,
+//    one running element-wise work or waiting on LDS while the other issues
+//    products. The workgroup walks 64-row tiles of Q and dO (every query head of
+//    the group) staged in LDS with their LSE and D, two buffers deep: the next
+//    tile's loads go out right after the barrier that publishes the current
+//    one and land while the current one is computed. The S / dP accumulators
+//    hold one key per lane and 16 rows per lane, which is the B-operand layout
+//    of the next products, so P and dS enter them as they are (rounded to the
+//    input dtype), with dO^T and Q^T read from the staged tiles by transposing
+//    LDS reads.
 //  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (batch, head);
 //    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
 //    of K and V staged in LDS (two buffers deep, as above): S^T = K Q^T,
 //    dP^T = V dO^T (one query row per lane), dS^T, then dQ^T += K^T dS^T with
-//    K^T from transposing reads.
+//    K^T from transposing reads. Its operands are read as the products need
+//    them, which keeps a wave within 256 registers: two workgroups share a CU
+//    (128 KiB of LDS), so each SIMD switches between two waves while one waits
+//    on LDS or its barrier (0.69 -> 0.42 ms on llm_prefill against one wave per
+//    SIMD with all operands read ahead in batches).
 // The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
 // instead of 5), which is what removes the atomics on dQ.
 #include "common.hpp"
@@ -35,10 +44,12 @@
 
 namespace mi355attn {
 
-constexpr int kBwdWaves = 4;
+constexpr int kBwdWaves = 4;                   // dQ workgroup
 constexpr int kBwdThreads = 64 * kBwdWaves;
-constexpr int kBwdKeysWG = 32 * kBwdWaves;  // keys per dK/dV workgroup
-constexpr int kBwdRowsWG = 32 * kBwdWaves;  // query rows per dQ workgroup
+constexpr int kDkdvWaves = 8;                  // dK/dV workgroup: 4 key blocks x 2 roles
+constexpr int kDkdvThreads = 64 * kDkdvWaves;
+constexpr int kBwdKeysWG = 32 * (kDkdvWaves / 2);  // keys per dK/dV workgroup
+constexpr int kBwdRowsWG = 32 * kBwdWaves;         // query rows per dQ workgroup
 constexpr int kBwdQT = 64;                  // query rows per dK/dV step
 constexpr int kBwdKT = 64;                  // keys per dQ step
 
@@ -59,18 +70,18 @@ __device__ __forceinline__ int bwd_swz(int row) {
 // Stages rows [r0, r0 + ROWS) of a [*, D] row-major tensor (rows >= n read as
 // zero) into an LDS tile: all threads of the workgroup take part, each load
 // moves 1 KiB.
-template <int D, int ROWS>
+template <int D, int ROWS, int NW>
 __device__ __forceinline__ void stage_rows(const uint16_t* base, int r0, int n, unsigned char* tile,
                                            int tid) {
   constexpr int ROW = D * 2, CH = D / 8, RPL = 64 / CH;
   constexpr int LOADS = ROWS / RPL;  // 1 KiB loads for the tile
-  static_assert(LOADS % kBwdWaves == 0, "loads split evenly over the waves");
+  static_assert(LOADS % NW == 0, "loads split evenly over the waves");
   const int wave = tid >> 6, lane = tid & 63;
   const int rows_valid = n - r0;  // > 0 for every staged tile
   const auto rs = make_rsrc(base + (int64_t)r0 * D, (uint32_t)rows_valid * ROW);
 #pragma unroll
-  for (int i = 0; i < LOADS / kBwdWaves; ++i) {
-    const int ld = wave * (LOADS / kBwdWaves) + i;
+  for (int i = 0; i < LOADS / NW; ++i) {
+    const int ld = wave * (LOADS / NW) + i;
     const int row = ld * RPL + lane / CH;
     const int pc = lane % CH;
     buf_load16_lds(rs, tile + ld * 1024, (uint32_t)row * ROW + (uint32_t)((pc ^ bwd_swz<D>(row)) << 4));
@@ -109,6 +120,22 @@ __device__ __forceinline__ u32x4_t tile_tr(const unsigned char* tile, int ks, in
   const u32x2_t lo = lds_read_tr16_staged((const lds_s16x4_t*)p1);
   const u32x2_t hi = lds_read_tr16_staged((const lds_s16x4_t*)p2);
   return (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+}
+
+// Workgroup L's (unit, block) pair. Consecutive workgroups go to the 8 XCDs in
+// turn, so with units % 8 == 0 each XCD is given a contiguous range of units
+// and walks the blocks of one unit after another: the workgroups resident on
+// an XCD share the staged rows of a few units in its L2 (spreading a unit's
+// blocks over all XCDs makes every L2 fetch every unit).
+__device__ __forceinline__ void bwd_block_of(int L, int units, int per_unit, int& unit, int& idx) {
+  if (units % 8 == 0) {
+    const int x = L % 8, s = L / 8;
+    unit = x * (units / 8) + s / per_unit;
+    idx = s % per_unit;
+  } else {
+    unit = L / per_unit;
+    idx = L % per_unit;
+  }
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
@@ -153,8 +180,20 @@ attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict
 
 // ---------------------------------------------------------------- dK, dV
 
+// Barrier between the two halves of a dK/dV step: the P values that the
+// first-role waves stored to LDS are complete and visible to the second-role
+// waves. Only LDS operations are waited for (the next stage's global loads stay
+// in flight), and the compiler fences keep memory accesses on their side.
+__device__ __forceinline__ void lds_exchange_barrier() {
+  wait_lgkmcnt0();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, 1)
+__global__ void __launch_bounds__(kDkdvThreads, 2)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
@@ -163,43 +202,53 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdQT * ROW;
   constexpr int STAGE = 2 * TILE + 2 * kBwdQT * 4;  // Q, dO, LSE, D
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int XCHG = kBwdKeysWG * kBwdQT * 4;     // P of one step (fp32)
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XCHG];
+  float* const xchg = reinterpret_cast<float*>(smem + 2 * STAGE);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Waves kb and kb + 4 (which share a SIMD) own the same 32 keys. The first
+  // computes S = Q K^T, P and dV; the second dP = dO V^T, dS = P (dP - D) and
+  // dK, taking P from the first through LDS. Each holds one of K, V and one of
+  // the two accumulators, and while one issues its products the other can run
+  // its element-wise work.
+  const int kb = wave & 3;
+  const bool second = wave >= 4;
   const int r32 = lane & 31, half = lane >> 5;
   const int nkt = (Nk + kBwdKeysWG - 1) / kBwdKeysWG;
-  const int kt = blockIdx.x % nkt;
-  const int unit = blockIdx.x / nkt;  // b * Hkv + g
+  // b * Hkv + g and its key block; the causally heaviest (first) blocks of a
+  // unit go first.
+  int unit, kt;
+  bwd_block_of(blockIdx.x, B * Hkv, nkt, unit, kt);
   const int b = unit / Hkv, g = unit % Hkv;
   const int group = Hq / Hkv;
   const int off = Nk - Nq;  // bottom-right causal alignment
   const int k0 = kt * kBwdKeysWG;
-  const int kw0 = k0 + 32 * wave;     // first key of this wave
-  const int my_key = kw0 + r32;       // this lane's key (column of S / dP)
+  const int kw0 = k0 + 32 * kb;   // first key of this wave
+  const int my_key = kw0 + r32;   // this lane's key (column of S / dP)
 
-  // K and V rows of the wave's keys as B operands: lane key r32, chunk
-  // half*DS + ds (keys >= Nk read as zero).
+  // K rows (first role) or V rows (second role) of the wave's keys as B
+  // operands: lane key r32, chunk half*DS + ds (keys >= Nk read as zero).
   const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
-  u32x4_t kf[DS], vf[DS];
+  u32x4_t bf[DS];
   {
     const int valid = max(0, min(32, Nk - kw0));
-    const auto rk = make_rsrc(k + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
-    const auto rv = make_rsrc(v + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
+    const auto rs = make_rsrc((second ? v : k) + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const uint32_t o16 = (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4);
-      kf[ds] = buf_load16(rk, o16);
-      vf[ds] = buf_load16(rv, o16);
-    }
+    for (int ds = 0; ds < DS; ++ds)
+      bf[ds] = buf_load16(rs, (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4));
   }
-  f32x16_t dka[DB], dva[DB];
+  // dV^T (first role) or dK^T (second role): d x this wave's 32 keys.
+  f32x16_t acc[DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) {
-    dka[db] = (f32x16_t){};
-    dva[db] = (f32x16_t){};
-  }
+  for (int db = 0; db < DB; ++db) acc[db] = (f32x16_t){};
   const float c = scale * kLog2e;
+  // This lane's P values of row block rb in the exchange buffer: four 16-byte
+  // pieces, each piece of the 64 lanes contiguous.
+  auto xchg_at = [&](int rb, int part) {
+    return reinterpret_cast<f32x4_t*>(xchg + (((kb * 2 + rb) * 4 + part) * 64 + lane) * 4);
+  };
 
   // Steps: every query head of the group, its 64-row tiles from the first one
   // whose rows may see a key of this workgroup (i >= k0 - off when causal).
@@ -215,8 +264,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const int r0 = (t_begin + i % per_head) * kBwdQT;
     const int64_t qoff = ((int64_t)b * Hq + h) * (int64_t)Nq;
     unsigned char* st = smem + (i & 1) * STAGE;
-    stage_rows<D, kBwdQT>(q + qoff * D, r0, Nq, st, tid);
-    stage_rows<D, kBwdQT>(dout + qoff * D, r0, Nq, st + TILE, tid);
+    stage_rows<D, kBwdQT, kDkdvWaves>(q + qoff * D, r0, Nq, st, tid);
+    stage_rows<D, kBwdQT, kDkdvWaves>(dout + qoff * D, r0, Nq, st + TILE, tid);
     if (wave == 0) stage_floats64(lse + qoff, r0, Nq, (float*)(st + 2 * TILE), lane);
     if (wave == 1) stage_floats64(delta + qoff, r0, Nq, (float*)(st + 2 * TILE) + kBwdQT, lane);
   };
@@ -224,8 +273,8 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   for (int i = 0; i < n_steps; ++i) {
     const int r0 = (t_begin + i % per_head) * kBwdQT;
     // Step i's loads (this wave's) have landed; the barrier publishes every
-    // wave's and also ends all reads of step i-1, whose buffer the loads of
-    // step i+1 reuse.
+    // wave's and also ends all reads of step i-1 (its stage, whose buffer the
+    // loads of step i+1 reuse, and the exchange buffer).
     wait_all_memory();
     __syncthreads();
     if (i + 1 < n_steps) issue(i + 1);
@@ -235,86 +284,115 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     const float* slse = (const float*)(st + 2 * TILE);
     const float* sdl = slse + kBwdQT;
 
+    if (!second) {
+      // S = Q K^T for the step's 64 rows x 32 keys, P = exp(scale S - LSE)
+      // (0 where masked), stored for the partner and kept packed for dV.
+      u32x4_t pf[2][2];
 #pragma unroll
-    for (int rb = 0; rb < kBwdQT / 32; ++rb) {
-      // Operands are read as whole batches ahead of their MFMA chains (one LDS
-      // latency per batch instead of one per product): the row operands of S
-      // and dP, then the transposed operands of dV and dK, whose latency hides
-      // behind the S / dP products and the element-wise work.
-      u32x4_t qa[DS], da[DS], ta[2 * DB], tb[2 * DB];
+      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+        u32x4_t qa[DS];
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        qa[ds] = tile_row16<D>(tq, 32 * rb + r32, half * DS + ds);
-        da[ds] = tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds);
-      }
+        for (int ds = 0; ds < DS; ++ds) qa[ds] = tile_row16<D>(tq, 32 * rb + r32, half * DS + ds);
+        __builtin_amdgcn_sched_barrier(0);
+        f32x16_t sacc = (f32x16_t){};
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int ds = 0; ds < DS; ++ds) sacc = mfma32x32x16<DT>(qa[ds], bf[ds], sacc);
+        float p[16];
 #pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          ta[ks * DB + db] = tile_tr<D>(tdo, 2 * rb + ks, db, lane);
-          tb[ks * DB + db] = tile_tr<D>(tq, 2 * rb + ks, db, lane);
+        for (int gq = 0; gq < 4; ++gq) {
+          // this lane's rows 32rb + 8gq + 4half + 0..3
+          const int lr = 32 * rb + 8 * gq + 4 * half;
+          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + lr);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int e = 4 * gq + x;
+            const int row = r0 + lr + x;
+            const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
+            p[e] = ok ? fast_exp2(__builtin_fmaf(sacc[e], c, -l4[x] * kLog2e)) : 0.f;
+          }
+          *xchg_at(rb, gq) = (f32x4_t){p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]};
         }
-      __builtin_amdgcn_sched_barrier(0);
-      // S = Q K^T and dP = dO V^T for 32 rows x this wave's 32 keys.
-      f32x16_t s = (f32x16_t){}, dp = (f32x16_t){};
 #pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        s = mfma32x32x16<DT>(qa[ds], kf[ds], s);
-        dp = mfma32x32x16<DT>(da[ds], vf[ds], dp);
+        for (int ks = 0; ks < 2; ++ks)
+          pf[rb][ks] = (u32x4_t){pack2<DT>(p[8 * ks + 0], p[8 * ks + 1]), pack2<DT>(p[8 * ks + 2], p[8 * ks + 3]),
+                                 pack2<DT>(p[8 * ks + 4], p[8 * ks + 5]), pack2<DT>(p[8 * ks + 6], p[8 * ks + 7])};
       }
-      float p[16], dsv[16];
+      lds_exchange_barrier();
+      // dV^T += dO^T P over the 64 rows.
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        // this lane's rows 32rb + 8gq + 4half + 0..3: LSE and D from LDS
-        const int lr = 32 * rb + 8 * gq + 4 * half;
-        const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + lr);
-        const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(sdl + lr);
+      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+        u32x4_t ta[2 * DB];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int e = 4 * gq + x;
-          const int row = r0 + lr + x;
-          const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
-          p[e] = ok ? fast_exp2(__builtin_fmaf(s[e], c, -l4[x] * kLog2e)) : 0.f;
-          dsv[e] = p[e] * (dp[e] - d4[x]);
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) ta[ks * DB + db] = tile_tr<D>(tdo, 2 * rb + ks, db, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(ta[ks * DB + db], pf[rb][ks], acc[db]);
+      }
+    } else {
+      // dP = dO V^T for the step's 64 rows x 32 keys.
+      f32x16_t dp[2];
+#pragma unroll
+      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+        u32x4_t da[DS];
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) da[ds] = tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds);
+        __builtin_amdgcn_sched_barrier(0);
+        dp[rb] = (f32x16_t){};
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) dp[rb] = mfma32x32x16<DT>(da[ds], bf[ds], dp[rb]);
+      }
+      lds_exchange_barrier();
+      // dS = P (dP - D) with the partner's P (same lane and slot layout as dP),
+      // then dK^T += Q^T dS.
+#pragma unroll
+      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+        u32x4_t tb[2 * DB];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) tb[ks * DB + db] = tile_tr<D>(tq, 2 * rb + ks, db, lane);
+        float dsv[16];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int lr = 32 * rb + 8 * gq + 4 * half;
+          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(sdl + lr);
+          const f32x4_t p4 = *xchg_at(rb, gq);
+#pragma unroll
+          for (int x = 0; x < 4; ++x) dsv[4 * gq + x] = p4[x] * (dp[rb][4 * gq + x] - d4[x]);
         }
+        u32x4_t sf[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          sf[ks] = (u32x4_t){pack2<DT>(dsv[8 * ks + 0], dsv[8 * ks + 1]),
+                             pack2<DT>(dsv[8 * ks + 2], dsv[8 * ks + 3]),
+                             pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
+                             pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(tb[ks * DB + db], sf[ks], acc[db]);
       }
-      u32x4_t pf[2], sf[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        pf[ks] = (u32x4_t){pack2<DT>(p[8 * ks + 0], p[8 * ks + 1]), pack2<DT>(p[8 * ks + 2], p[8 * ks + 3]),
-                           pack2<DT>(p[8 * ks + 4], p[8 * ks + 5]), pack2<DT>(p[8 * ks + 6], p[8 * ks + 7])};
-        sf[ks] = (u32x4_t){pack2<DT>(dsv[8 * ks + 0], dsv[8 * ks + 1]),
-                           pack2<DT>(dsv[8 * ks + 2], dsv[8 * ks + 3]),
-                           pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
-                           pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
-      }
-      // dV^T += dO^T P, dK^T += Q^T dS (d x keys) over these 32 rows.
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          dva[db] = mfma32x32x16<DT>(ta[ks * DB + db], pf[ks], dva[db]);
-          dka[db] = mfma32x32x16<DT>(tb[ks * DB + db], sf[ks], dka[db]);
-        }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
 
-  // dK = scale * (dK^T)^T, dV = (dV^T)^T: lane key r32, d = 32db + 8(e/4) + 4half + e%4.
+  // dV = (dV^T)^T, dK = scale * (dK^T)^T: lane key r32, d = 32db + 8(e/4) + 4half + e%4.
   if (my_key < Nk) {
-    uint16_t* pk = dk + kvoff + (int64_t)my_key * D;
-    uint16_t* pv = dv + kvoff + (int64_t)my_key * D;
+    const float f = second ? scale : 1.f;
+    uint16_t* po = (second ? dk : dv) + kvoff + (int64_t)my_key * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d0 = 32 * db + 8 * gq + 4 * half;
-        *reinterpret_cast<u32x2_t*>(pk + d0) =
-            (u32x2_t){pack2<DT>(dka[db][4 * gq + 0] * scale, dka[db][4 * gq + 1] * scale),
-                      pack2<DT>(dka[db][4 * gq + 2] * scale, dka[db][4 * gq + 3] * scale)};
-        *reinterpret_cast<u32x2_t*>(pv + d0) =
-            (u32x2_t){pack2<DT>(dva[db][4 * gq + 0], dva[db][4 * gq + 1]),
-                      pack2<DT>(dva[db][4 * gq + 2], dva[db][4 * gq + 3])};
+        *reinterpret_cast<u32x2_t*>(po + d0) =
+            (u32x2_t){pack2<DT>(acc[db][4 * gq + 0] * f, acc[db][4 * gq + 1] * f),
+                      pack2<DT>(acc[db][4 * gq + 2] * f, acc[db][4 * gq + 3] * f)};
       }
   }
 }
@@ -322,7 +400,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 // ---------------------------------------------------------------- dQ
 
 template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, 1)
+__global__ void __launch_bounds__(kBwdThreads, 2)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                    const float* __restrict__ lse, const float* __restrict__ delta,
@@ -336,8 +414,11 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, half = lane >> 5;
   const int nqt = (Nq + kBwdRowsWG - 1) / kBwdRowsWG;
-  const int qt = blockIdx.x % nqt;
-  const int unit = blockIdx.x / nqt;  // b * Hq + h
+  // b * Hq + h and its row block; the causally heaviest (last) blocks of a
+  // unit go first.
+  int unit, qt;
+  bwd_block_of(blockIdx.x, B * Hq, nqt, unit, qt);
+  if (CAUSAL) qt = nqt - 1 - qt;
   const int b = unit / Hq, h = unit % Hq;
   const int g = h / (Hq / Hkv);
   const int off = Nk - Nq;
@@ -374,8 +455,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
   auto issue = [&](int t) {
     unsigned char* st = smem + (t & 1) * STAGE;
-    stage_rows<D, kBwdKT>(k + kvoff, t * kBwdKT, Nk, st, tid);
-    stage_rows<D, kBwdKT>(v + kvoff, t * kBwdKT, Nk, st + TILE, tid);
+    stage_rows<D, kBwdKT, kBwdWaves>(k + kvoff, t * kBwdKT, Nk, st, tid);
+    stage_rows<D, kBwdKT, kBwdWaves>(v + kvoff, t * kBwdKT, Nk, st + TILE, tid);
   };
   if (n_tiles > 0) issue(0);
   for (int t = 0; t < n_tiles; ++t) {
@@ -389,32 +470,15 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const unsigned char* tv = tk + TILE;
 
     // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
-    // Operands are read as batches ahead of their MFMA chains: K and V rows of
-    // a key block, then the K^T operands of dQ, whose latency hides behind the
-    // products and the element-wise work.
     f32x16_t s[2], dp[2];
-    u32x4_t ta[4 * DB];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      u32x4_t ka[DS], va[DS];
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        ka[ds] = tile_row16<D>(tk, 32 * kb + r32, half * DS + ds);
-        va[ds] = tile_row16<D>(tv, 32 * kb + r32, half * DS + ds);
-      }
-      if (kb == 1) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) ta[ks * DB + db] = tile_tr<D>(tk, ks, db, lane);
-      }
-      __builtin_amdgcn_sched_barrier(0);
       s[kb] = (f32x16_t){};
       dp[kb] = (f32x16_t){};
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        s[kb] = mfma32x32x16<DT>(ka[ds], qf[ds], s[kb]);
-        dp[kb] = mfma32x32x16<DT>(va[ds], dof[ds], dp[kb]);
+        s[kb] = mfma32x32x16<DT>(tile_row16<D>(tk, 32 * kb + r32, half * DS + ds), qf[ds], s[kb]);
+        dp[kb] = mfma32x32x16<DT>(tile_row16<D>(tv, 32 * kb + r32, half * DS + ds), dof[ds], dp[kb]);
       }
     }
     // dS^T, packed as the B operand of dQ^T += K^T dS^T (4 steps of 16 keys).
@@ -437,8 +501,8 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) dqa[db] = mfma32x32x16<DT>(ta[ks * DB + db], sf[ks], dqa[db]);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sf[ks], dqa[db]);
   }
 
   // dQ = scale * (dQ^T)^T: lane row r32, d = 32db + 8(e/4) + 4half + e%4.
@@ -472,7 +536,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, DT);
   const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
-                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     dim3(kDkdvThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
   const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
