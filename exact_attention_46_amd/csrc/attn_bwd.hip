@@ -39,6 +39,8 @@
 //    SIMD with all operands read ahead in batches).
 // The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
 // instead of 5), which is what removes the atomics on dQ.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -270,23 +272,32 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
     if (wave == 1) stage_floats64(delta + qoff, r0, Nq, (float*)(st + 2 * TILE) + kBwdQT, lane);
   };
   if (n_steps > 0) issue(0);
-  for (int i = 0; i < n_steps; ++i) {
-    const int r0 = (t_begin + i % per_head) * kBwdQT;
-    // Step i's loads (this wave's) have landed; the barrier publishes every
-    // wave's and also ends all reads of step i-1 (its stage, whose buffer the
-    // loads of step i+1 reuse, and the exchange buffer).
+  // Start of step i: its loads (this wave's) have landed; the barrier
+  // publishes every wave's and also ends all reads of step i-1 (its stage,
+  // whose buffer the loads of step i+1 reuse, and the exchange buffer).
+  auto begin_step = [&](int i) {
     wait_all_memory();
     __syncthreads();
     if (i + 1 < n_steps) issue(i + 1);
-    const unsigned char* st = smem + (i & 1) * STAGE;
-    const unsigned char* tq = st;
-    const unsigned char* tdo = st + TILE;
-    const float* slse = (const float*)(st + 2 * TILE);
-    const float* sdl = slse + kBwdQT;
-
-    if (!second) {
-      // S = Q K^T for the step's 64 rows x 32 keys, P = exp(scale S - LSE)
-      // (0 where masked), stored for the partner and kept packed for dV.
+  };
+  // Whether any (row, key) pair of step i and this wave's keys is masked:
+  // rows past Nq, keys past Nk, or (causal) a key after some row's diagonal.
+  auto needs_mask = [&](int r0) {
+    return r0 + kBwdQT > Nq || kw0 + 32 > Nk || (CAUSAL && kw0 + 31 > r0 + off);
+  };
+  // Each role runs its own copy of the step loop, and each step is compiled
+  // for both stage buffers, so every LDS address is a per-lane base set up
+  // once plus an immediate offset.
+  if (!second) {
+    // S = Q K^T for the step's 64 rows x 32 keys, P = exp(scale S - LSE) (0
+    // where masked), stored for the partner and kept packed for dV^T += dO^T P.
+    auto step = [&](auto buf_c, int i) {
+      constexpr int BUF = decltype(buf_c)::value;
+      const int r0 = (t_begin + i % per_head) * kBwdQT;
+      const bool masked = needs_mask(r0);
+      const unsigned char* tq = smem + BUF * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const float* slse = (const float*)(tq + 2 * TILE);
       u32x4_t pf[2][2];
 #pragma unroll
       for (int rb = 0; rb < kBwdQT / 32; ++rb) {
@@ -306,9 +317,15 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int e = 4 * gq + x;
-            const int row = r0 + lr + x;
-            const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
-            p[e] = ok ? fast_exp2(__builtin_fmaf(sacc[e], c, -l4[x] * kLog2e)) : 0.f;
+            p[e] = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[x] * kLog2e));
+          }
+          if (masked) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const int row = r0 + lr + x;
+              const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
+              p[4 * gq + x] = ok ? p[4 * gq + x] : 0.f;
+            }
           }
           *xchg_at(rb, gq) = (f32x4_t){p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]};
         }
@@ -318,7 +335,6 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                                  pack2<DT>(p[8 * ks + 4], p[8 * ks + 5]), pack2<DT>(p[8 * ks + 6], p[8 * ks + 7])};
       }
       lds_exchange_barrier();
-      // dV^T += dO^T P over the 64 rows.
 #pragma unroll
       for (int rb = 0; rb < kBwdQT / 32; ++rb) {
         u32x4_t ta[2 * DB];
@@ -332,8 +348,25 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(ta[ks * DB + db], pf[rb][ks], acc[db]);
       }
-    } else {
-      // dP = dO V^T for the step's 64 rows x 32 keys.
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int i = 0; i < n_steps; i += 2) {
+      begin_step(i);
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < n_steps) {
+        begin_step(i + 1);
+        step(std::integral_constant<int, 1>{}, i + 1);
+      }
+    }
+  } else {
+    // dP = dO V^T for the step's 64 rows x 32 keys; dS = P (dP - D) with the
+    // partner's P (same lane and slot layout as dP), then dK^T += Q^T dS.
+    auto step = [&](auto buf_c, int i) {
+      constexpr int BUF = decltype(buf_c)::value;
+      const unsigned char* tq = smem + BUF * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const float* sdl = (const float*)(tq + 2 * TILE) + kBwdQT;
+      (void)i;
       f32x16_t dp[2];
 #pragma unroll
       for (int rb = 0; rb < kBwdQT / 32; ++rb) {
@@ -346,8 +379,6 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
         for (int ds = 0; ds < DS; ++ds) dp[rb] = mfma32x32x16<DT>(da[ds], bf[ds], dp[rb]);
       }
       lds_exchange_barrier();
-      // dS = P (dP - D) with the partner's P (same lane and slot layout as dP),
-      // then dK^T += Q^T dS.
 #pragma unroll
       for (int rb = 0; rb < kBwdQT / 32; ++rb) {
         u32x4_t tb[2 * DB];
@@ -377,8 +408,16 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 #pragma unroll
           for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(tb[ks * DB + db], sf[ks], acc[db]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int i = 0; i < n_steps; i += 2) {
+      begin_step(i);
+      step(std::integral_constant<int, 0>{}, i);
+      if (i + 1 < n_steps) {
+        begin_step(i + 1);
+        step(std::integral_constant<int, 1>{}, i + 1);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 
   // dV = (dV^T)^T, dK = scale * (dK^T)^T: lane key r32, d = 32db + 8(e/4) + 4half + e%4.
