@@ -497,15 +497,16 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     stage_rows<D, kBwdKT, kBwdWaves>(k + kvoff, t * kBwdKT, Nk, st, tid);
     stage_rows<D, kBwdKT, kBwdWaves>(v + kvoff, t * kBwdKT, Nk, st + TILE, tid);
   };
-  if (n_tiles > 0) issue(0);
-  for (int t = 0; t < n_tiles; ++t) {
+  // Each tile is compiled for both stage buffers (every LDS address a per-lane
+  // base set up once plus an immediate offset); masking only where a tile
+  // straddles this wave's diagonal or a ragged edge, and no products for a
+  // tile wholly above the diagonal.
+  auto step = [&](auto buf_c, int t) {
+    constexpr int BUF = decltype(buf_c)::value;
     const int k0 = t * kBwdKT;
-    // Tile t has landed (this wave's loads; the barrier publishes the rest and
-    // ends all reads of tile t-1, whose buffer tile t+1 reuses).
-    wait_all_memory();
-    __syncthreads();
-    if (t + 1 < n_tiles) issue(t + 1);
-    const unsigned char* tk = smem + (t & 1) * STAGE;
+    if (CAUSAL && k0 > qw0 + 31 + off) return;
+    const bool masked = qw0 + 32 > Nq || k0 + kBwdKT > Nk || (CAUSAL && k0 + kBwdKT - 1 > qw0 + off);
+    const unsigned char* tk = smem + BUF * STAGE;
     const unsigned char* tv = tk + TILE;
 
     // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
@@ -526,12 +527,17 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     for (int kb = 0; kb < 2; ++kb) {
       float x[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
-        const bool ok = row_ok && key < Nk && (!CAUSAL || key <= my_row + off);
-        const float p = ok ? fast_exp2(__builtin_fmaf(s[kb][e], c, -l2)) : 0.f;
-        x[e] = p * (dp[kb][e] - dl);
+      for (int e = 0; e < 16; ++e) x[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, -l2));
+      if (masked) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
+          const bool ok = row_ok && key < Nk && (!CAUSAL || key <= my_row + off);
+          x[e] = ok ? x[e] : 0.f;
+        }
       }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = x[e] * (dp[kb][e] - dl);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         sf[2 * kb + j] = (u32x4_t){pack2<DT>(x[8 * j + 0], x[8 * j + 1]), pack2<DT>(x[8 * j + 2], x[8 * j + 3]),
@@ -542,6 +548,23 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 #pragma unroll
       for (int db = 0; db < DB; ++db)
         dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sf[ks], dqa[db]);
+  };
+  // Start of tile t: its loads (this wave's) have landed; the barrier
+  // publishes the rest and ends all reads of tile t-1, whose buffer tile t+1
+  // reuses.
+  auto begin_tile = [&](int t) {
+    wait_all_memory();
+    __syncthreads();
+    if (t + 1 < n_tiles) issue(t + 1);
+  };
+  if (n_tiles > 0) issue(0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    begin_tile(t);
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) {
+      begin_tile(t + 1);
+      step(std::integral_constant<int, 1>{}, t + 1);
+    }
   }
 
   // dQ = scale * (dQ^T)^T: lane row r32, d = 32db + 8(e/4) + 4half + e%4.
