@@ -432,6 +432,9 @@ BWD = [
     (1, 4, 1, 257, 257, 64, "bf16", False),
     (1, 4, 4, 1000, 1000, 128, "bf16", True),
     (1, 4, 4, 2048, 2048, 128, "bf16", True),
+    # 8 and 16 (batch, head) units: the XCD-contiguous block order of both
+    # gradient kernels, with GQA and a ragged length
+    (2, 8, 4, 333, 333, 128, "bf16", True),
 ]
 
 
@@ -467,6 +470,32 @@ def test_backward(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     _check_grad(outs[0][1], rq, dtype, tag + " dq")
     _check_grad(outs[1][1], rk, dtype, tag + " dk")
     _check_grad(outs[2][1], rv, dtype, tag + " dv")
+
+
+def test_backward_full_size_sampled_heads():
+    """The backward on the whole llm_prefill workload, in the launch configuration
+    the benchmark times; three (batch, head) slices, first and last included, are
+    checked against the oracle's backward of that head alone (heads are independent
+    when Hq == Hkv)."""
+    w = wl.WORKLOADS["llm_prefill"]
+    assert w.Hq == w.Hkv
+    q, k, v = wl.workload_prefill_inputs(w)
+    g = torch.Generator().manual_seed(w.seed + 7)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = ea.fwd(qd, kd, vd, causal=True, scale=w.scale)
+    dq, dk, dv = ea.bwd(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    picks = [(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))]
+    for b, h in picks:
+        sl = lambda t: t[b:b + 1, h:h + 1].contiguous()
+        rq, rk, rv = oracle.attn_bwd(wl.bits(sl(q)), wl.bits(sl(k)), wl.bits(sl(v)),
+                                     wl.bits(sl(do)), wl.DTYPE_CODE[w.dtype], w.scale, True)
+        tag = "bwd llm_prefill b=%d h=%d" % (b, h)
+        _check_grad(sl(dq.cpu()), rq, w.dtype, tag + " dq")
+        _check_grad(sl(dk.cpu()), rk, w.dtype, tag + " dk")
+        _check_grad(sl(dv.cpu()), rv, w.dtype, tag + " dv")
 
 
 # --------------------------------------------------------------- one-call decode (library chunk)
