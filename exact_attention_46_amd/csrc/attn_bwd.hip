@@ -10,8 +10,7 @@
 //   dV_j  = sum_i P_ij dO_i,   dK_j = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 // dK and dV of kv-head g sum over the query heads that read it (GQA).
 //
-// Three kernels on one stream, no atomics (the result is deterministic):
-//  * attn_bwd_delta_kernel: D for every query row.
+// Two kernels on one stream, no atomics (the result is deterministic):
 //  * attn_bwd_dkdv_kernel: one workgroup of 8 waves per (batch, kv-head, 128
 //    keys). Two waves own each 32 keys: the first keeps their K rows in
 //    registers, computes S = Q K^T and P and accumulates dV^T += dO^T P; the
@@ -32,7 +31,9 @@
 //    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
 //    of K and V staged in LDS (two buffers deep, as above): S^T = K Q^T,
 //    dP^T = V dO^T (one query row per lane), dS^T, then dQ^T += K^T dS^T with
-//    K^T from transposing reads. Its operands are read as the products need
+//    K^T from transposing reads. It runs first and also computes D for its
+//    rows (from their dO and O rows, each lane pair summing half of d), which
+//    the dK/dV kernel then reads. Its operands are read as the products need
 //    them, which keeps a wave within 256 registers: two workgroups share a CU
 //    (128 KiB of LDS), so each SIMD switches between two waves while one waits
 //    on LDS or its barrier (0.69 -> 0.42 ms on llm_prefill against one wave per
@@ -140,44 +141,17 @@ __device__ __forceinline__ void bwd_block_of(int L, int units, int per_unit, int
   }
 }
 
-// ---------------------------------------------------------------- D = rowsum(dO * O)
-
-template <int D>
-__global__ void __launch_bounds__(256)
-attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
-                      float* __restrict__ delta, int64_t rows, int dt) {
-  // 16 lanes per row, 8 elements (16 bytes) per lane at d = 128, 4 at d = 64.
-  constexpr int PER = D / 16;
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
-  float acc = 0.f;
-  if (row < rows) {
-    const uint16_t* po = o + row * D + sub * PER;
-    const uint16_t* pd = dout + row * D + sub * PER;
-#pragma unroll
-    for (int i = 0; i < PER; i += 2) {
-      const uint32_t wo = *reinterpret_cast<const uint32_t*>(po + i);
-      const uint32_t wd = *reinterpret_cast<const uint32_t*>(pd + i);
-      float o0, o1, d0, d1;
-      if (dt == kBF16) {
-        o0 = __uint_as_float(wo << 16);
-        o1 = __uint_as_float(wo & 0xffff0000u);
-        d0 = __uint_as_float(wd << 16);
-        d1 = __uint_as_float(wd & 0xffff0000u);
-      } else {
-        const f16x2_t ho = __builtin_bit_cast(f16x2_t, wo), hd = __builtin_bit_cast(f16x2_t, wd);
-        o0 = (float)ho[0];
-        o1 = (float)ho[1];
-        d0 = (float)hd[0];
-        d1 = (float)hd[1];
-      }
-      acc = __builtin_fmaf(o0, d0, acc);
-      acc = __builtin_fmaf(o1, d1, acc);
-    }
+// acc + a.x b.x + a.y b.y for two packed pairs of the input dtype (products exact
+// in fp32).
+template <int DT>
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), acc, false);
+  } else {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b),
+                                  acc, false);
   }
-#pragma unroll
-  for (int sh = 8; sh >= 1; sh >>= 1) acc += __shfl_xor(acc, sh, 16);
-  if (row < rows && sub == 0) delta[row] = acc;
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -235,7 +209,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
   u32x4_t bf[DS];
   {
-    const int valid = max(0, min(32, Nk - kw0));
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nk - kw0)));
     const auto rs = make_rsrc((second ? v : k) + kvoff + (int64_t)kw0 * D, (uint32_t)valid * ROW);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds)
@@ -441,9 +415,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kBwdThreads, 2)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-                   const float* __restrict__ lse, const float* __restrict__ delta,
-                   uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk, float scale) {
+                   const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+                   const uint16_t* __restrict__ dout, const float* __restrict__ lse,
+                   float* __restrict__ delta, uint16_t* __restrict__ dq, int B, int Hq, int Hkv,
+                   int Nq, int Nk, float scale) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdKT * ROW;
   constexpr int STAGE = 2 * TILE;  // K, V
@@ -470,7 +445,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // Q^T and dO^T B operands: lane row r32, chunk half*DS + ds (rows >= Nq zero).
   u32x4_t qf[DS], dof[DS];
   {
-    const int valid = max(0, min(32, Nq - qw0));
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)));
     const auto rq = make_rsrc(q + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
     const auto rd = make_rsrc(dout + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
 #pragma unroll
@@ -482,7 +457,22 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
   const bool row_ok = my_row < Nq;
   const float l2 = row_ok ? lse[qrow0 + my_row] * kLog2e : 0.f;
-  const float dl = row_ok ? delta[qrow0 + my_row] : 0.f;
+  // D of this lane's row, sum_t dO_t O_t: each lane of the pair (l, l ^ 32)
+  // sums its half of d; the first-half lane stores D for the dK/dV kernel.
+  float dl;
+  {
+    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)));
+    const auto ro = make_rsrc(o + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
+    float acc = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const u32x4_t ov = buf_load16(ro, (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = dot2_acc<DT>(ov[j], dof[ds][j], acc);
+    }
+    dl = sum_with_partner32(acc);
+    if (row_ok && half == 0) delta[qrow0 + my_row] = dl;
+  }
   const float c = scale * kLog2e;
   f32x16_t dqa[DB];
 #pragma unroll
@@ -587,25 +577,22 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
 int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk) {
   const int64_t a = (int64_t)B * Hkv * ((Nk + kBwdKeysWG - 1) / kBwdKeysWG);
   const int64_t c = (int64_t)B * Hq * ((Nq + kBwdRowsWG - 1) / kBwdRowsWG);
-  const int64_t r = ((int64_t)B * Hq * Nq + 15) / 16;
-  return a > c ? (a > r ? a : r) : (c > r ? c : r);
+  return a > c ? a : c;
 }
 
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
-  hipLaunchKernelGGL((attn_bwd_delta_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0,
-                     stream, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows, DT);
+  // dQ first: it also writes D, which the dK/dV kernel reads.
+  const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt)),
+                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
+                     a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
   const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
                      dim3(kDkdvThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
-  const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt)),
-                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
-                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                     (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
   return hipGetLastError();
 }
 

@@ -127,9 +127,9 @@ int attn_fwd_local(const void* q, const void* k, const void* v, void* o, float* 
  *   dk, dv     [B, Hkv, Nk, d]  dtype  (written, rounded to nearest even)
  *
  * Shapes, head mapping, causal alignment, d, dtype and scale as in attn_fwd. A
- * query row with no allowed key contributes nothing and gets dq = 0. Three
- * kernels run in order on `stream`; the result does not depend on scheduling
- * (no atomics).
+ * query row with no allowed key contributes nothing and gets dq = 0. Two
+ * kernels run in order on `stream` (dq, which also writes delta, then dk and
+ * dv); the result does not depend on scheduling (no atomics).
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
