@@ -264,7 +264,7 @@ def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
     tf = flops / (ms * 1e-3) / 1e12
     return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
             "flop_convention": "2.5 x forward (causal halved)",
-            "roofline": {"kernel": "attn_bwd (delta + dkdv + dq kernels)", "bound": "mfma",
+            "roofline": {"kernel": "attn_bwd (dq + dkdv kernels)", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
