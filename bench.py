@@ -65,6 +65,8 @@ def parse():
                     help="skip the one-call decode (library chunk) measurement")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-cache decode measurement")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the forward on the GQA-prefill and long-context workloads")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="restrict the timed step (for per-kernel profiles)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -303,6 +305,38 @@ def bench_local(args, torch, np, ea, wp, qg, kg, vg, stream):
                          "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
 
 
+def bench_fwd_workload(args, torch, np, ea, wl, name, dev, stream):
+    """The causal forward on another prefill workload (inputs built like the
+    step's), timed in a loop of its own after the steps."""
+    print("bench: forward on %s" % name, file=sys.stderr, flush=True)
+    w = wl.WORKLOADS[name]
+    q, k, v = (t.to(dev) for t in wl.workload_prefill_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    def run():
+        ea.attn_fwd(q, k, v, o, lse, True, w.scale, stream)
+
+    steps = max(1, min(args.steps, 20))
+    for _ in range(max(1, min(args.warmup, 5))):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    flops = 4.0 * w.B * w.Hq * w.N * w.N * w.d / 2
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+            "shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": True},
+            "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal>", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+
+
 def bench_qkvpacked(args, torch, np, ea, wp, stream):
     """The llm_prefill attention read from one packed [B, N, 3, H, d] tensor (no
     permute) with o written [B, N, H, d]. Timed in a loop of its own."""
@@ -537,6 +571,11 @@ def main():
         out["fwd_qkvpacked"] = bench_qkvpacked(args, torch, np, ea, wp, stream)
     if do_pre and not args.no_varlen:
         out["fwd_varlen"] = bench_varlen(args, torch, np, ea, wl, dev, stream)
+    if do_pre and not args.no_configs:
+        out["fwd_gqa_prefill"] = bench_fwd_workload(args, torch, np, ea, wl, "gqa_prefill", dev,
+                                                    stream)
+        out["fwd_long_context"] = bench_fwd_workload(args, torch, np, ea, wl, "long_context",
+                                                     dev, stream)
     if do_dec and not args.no_auto:
         out["decode_auto"] = bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc,
                                                stream)
