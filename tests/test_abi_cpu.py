@@ -85,6 +85,26 @@ def test_attn_fwd_rejects(lib, kw, code):
     assert fwd(lib, **kw) == code
 
 
+def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A2, delta=A2, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2,
+        Nq=8, Nk=8, d=128, scale=0.1, causal=1, dtype=0):
+    return lib.attn_bwd(q, k, v, o, do, lse, delta, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                        causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(do=None), -1), (dict(lse=None), -1),
+    (dict(delta=None), -1), (dict(dq=None), -1), (dict(dk=None), -1), (dict(dv=None), -1),
+    (dict(B=0), -2), (dict(Hkv=0), -2), (dict(Nq=0), -2), (dict(Nk=-3), -2),
+    (dict(Hq=3, Hkv=2), -2), (dict(Nq=2**23 + 1), -2),
+    (dict(B=2**20, Hq=2**10, Hkv=2**10, Nq=128 * 4), -2),
+    (dict(d=32), -3), (dict(dtype=5), -3),
+    (dict(scale=0.0), -5), (dict(scale=float("nan")), -5), (dict(causal=-1), -5),
+    (dict(do=MIS), -4), (dict(dk=MIS), -4), (dict(delta=ctypes.c_void_p(4099)), -4),
+])
+def test_attn_bwd_rejects(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
 def fwd_varlen(lib, q=A, k=A, v=A, o=A2, lse=A2, cq=A, ck=A2, B=3, Hq=4, Hkv=2, total_q=100,
                total_k=120, max_q=60, d=128, scale=0.1, causal=1, dtype=0):
     return lib.attn_fwd_varlen(q, k, v, o, lse, cq, ck, B, Hq, Hkv, total_q, total_k, max_q, d,
