@@ -48,7 +48,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first (the clocks settle within a few hundred)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle timing (used for profiler runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -318,7 +319,7 @@ def bench_fwd_workload(args, torch, np, ea, wl, name, dev, stream):
         ea.attn_fwd(q, k, v, o, lse, True, w.scale, stream)
 
     steps = max(1, min(args.steps, 20))
-    for _ in range(max(1, min(args.warmup, 5))):
+    for _ in range(max(1, min(args.warmup, 50))):
         run()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
