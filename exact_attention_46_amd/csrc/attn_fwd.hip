@@ -105,6 +105,7 @@ constexpr int kFwdL2Units = 8;
 // units, so every XCD gets the same share of every sequence (a contiguous block
 // of units per XCD would hand whole long sequences to a few XCDs); all query
 // tiles of a unit still land on one XCD when the unit count is a multiple of 8.
+// Token-major batches of equal lengths (packed QKV) keep the contiguous order.
 __device__ __forceinline__ void fwd_tile_of(int L, int units, int nqt, int group, int causal,
                                             bool spread, int& unit, int& qtile) {
   constexpr int G = kFwdL2Units;
@@ -182,7 +183,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const int nqt = (Nq + kFwdBM - 1) / kFwdBM;
   const int group = Hq / Hkv;
   int unit, qtile;
-  fwd_tile_of(blockIdx.x, B * Hq, nqt, group, CAUSAL ? 1 : 0, VARLEN, unit, qtile);
+  fwd_tile_of(blockIdx.x, B * Hq, nqt, group, CAUSAL ? 1 : 0, VARLEN && vl.cu_q != nullptr, unit,
+              qtile);
   const int b = unit / Hq;
   const int h = unit % Hq;
   const int g = h / group;  // == floor(h * Hkv / Hq) since Hq % Hkv == 0
