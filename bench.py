@@ -175,6 +175,7 @@ def cpu_baseline(w, q, k, v, target_s):
 
     qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
     rng = np.random.default_rng(12345)
+    cores = oracle.max_threads()  # the oracle keeps the last thread count it was given
 
     def sample(n):
         b = rng.integers(0, w.B, n)
@@ -184,7 +185,7 @@ def cpu_baseline(w, q, k, v, target_s):
 
     def run(rows):
         t0 = time.perf_counter()
-        oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows)
+        oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows, nthreads=cores)
         dt = time.perf_counter() - t0
         flops = float(np.sum(4.0 * (rows[:, 2] + 1) * w.d))  # metric convention, causal
         return dt, flops
@@ -193,10 +194,61 @@ def cpu_baseline(w, q, k, v, target_s):
     n = int(min(2_000_000, max(256, 256 * target_s / max(dt, 1e-3))))
     rows = sample(n)
     dt, fl = run(rows)
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(),
+    # the same oracle on one thread, on a sample of about a tenth of the time
+    rows1 = rows[: max(16, n // (10 * max(1, cores)))]
+    t0 = time.perf_counter()
+    oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows1, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    fl1 = float(np.sum(4.0 * (rows1[:, 2] + 1) * w.d))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": "%d seeded random query rows of the llm_prefill workload (exact fp64 "
                       "causal rows, avg %d keys), %.1f s" % (n, int(rows[:, 2].mean()) + 1, dt),
+            "seconds": dt,
+            "one_thread": {"value": fl1 / dt1 / 1e12, "unit": "TFLOP/s",
+                           "sample": "the first %d of those rows, %.1f s" % (len(rows1), dt1)},
+            "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_decode(wd, sl, dq, kc, vc, cores, n_seq=None):
+    """Times the fp64 decode oracle on the decode workload (all sequences unless
+    n_seq picks a seeded sample; every key of each); KV GB/s like the metric."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_46_amd import workloads as wl
+
+    rng = np.random.default_rng(777)
+    n_seq = dq.shape[0] if n_seq is None else n_seq
+    idx = np.sort(rng.choice(dq.shape[0], size=n_seq, replace=False))
+    lens = sl.numpy()[idx].astype(np.int64)
+    L = int(lens.max())
+    import torch
+
+    ti = torch.as_tensor(idx, dtype=torch.long, device=dq.device)
+    q = dq.index_select(0, ti).cpu()
+    k = kc.index_select(0, ti)[:, :, :L].cpu()
+    v = vc.index_select(0, ti)[:, :, :L].cpu()
+    t0 = time.perf_counter()
+    oracle.decode(wl.bits(q), wl.bits(k), wl.bits(v), lens.astype(np.int32), 0, wd.scale,
+                  nthreads=cores)
+    dt = time.perf_counter() - t0
+    kv = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d of the decode workload's %d sequences (%d keys in all, every "
+                      "query head), %.1f s" % (n_seq, dq.shape[0], int(lens.sum()), dt),
             "seconds": dt}
 
 
@@ -586,6 +638,9 @@ def main():
     if not args.no_cpu_baseline and do_pre:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wp, q, k, v, args.cpu_seconds)
+        if do_dec:
+            out["cpu_baseline"]["decode"] = cpu_baseline_decode(wd, sl, dq, kc, vc,
+                                                                out["cpu_baseline"]["cores"])
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
