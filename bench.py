@@ -607,10 +607,17 @@ def main():
         kv_bytes = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
         dec_ms = split_ms + comb_ms
         gbs = kv_bytes / (dec_ms * 1e-3) / 1e9
+        # every byte the two kernels must move: K/V, q, the partials (O fp32 + LSE of each
+        # valid chunk and query head, written then read), O and LSE
+        chunks = float(np.sum(-(-lens // wd.chunk)))
+        part = chunks * wd.Hq * (wd.d + 1) * 4
+        total_bytes = kv_bytes + dq.numel() * 2 + 2 * part + wd.B * wd.Hq * (wd.d * 2 + 4)
         out["decode"] = {"value": round(gbs, 1), "unit": "GB/s", "split_ms": round(split_ms, 4),
                          "combine_ms": round(comb_ms, 4),
                          "split_only_GBs": round(kv_bytes / (split_ms * 1e-3) / 1e9, 1),
                          "kv_bytes": int(kv_bytes),
+                         "total_bytes": int(total_bytes),
+                         "total_GBs": round(total_bytes / (dec_ms * 1e-3) / 1e9, 1),
                          "roofline": {"kernel": "attn_decode_split_kernel<bf16,128>",
                                       "bound": "hbm", "achieved": round(gbs, 1),
                                       "peak": PEAK_HBM_GBS, "unit": "GB/s",
