@@ -20,6 +20,13 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# A build instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (any out-of-bounds access, use after free or undefined operation aborts).
+# Loading it needs the ASan runtime first in the process (LD_PRELOAD), so the
+# tests use it from a child process that sets ORACLE_LIB to its path.
+_LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+_COMMON_FLAGS = ["-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+                 "-fno-fast-math", "-ffp-contract=off"]
 
 BF16 = 0
 FP16 = 1
@@ -31,18 +38,30 @@ def build(force: bool = True) -> str:
     """Compiles ``attn_oracle.c`` with gcc (fp64, OpenMP) into ``liboracle.so``."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", "-O2"] + _COMMON_FLAGS + [_SRC, "-o", tmp, "-lm"]
         subprocess.check_call(cmd)
         os.replace(tmp, _LIB)
     return _LIB
 
 
+def build_sanitized() -> str:
+    """Compiles ``attn_oracle.c`` with -fsanitize=address,undefined (errors
+    abort) into ``liboracle_san.so`` and returns its path."""
+    tmp = _LIB_SAN + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all"] + _COMMON_FLAGS + [_SRC, "-o", tmp, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB_SAN)
+    return _LIB_SAN
+
+
 def _load():
     global _lib
     if _lib is None:
-        build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("ORACLE_LIB")
+        if not path:
+            path = build(force=False)
+        lib = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i = ctypes.c_int
         i64 = ctypes.c_int64
