@@ -14,6 +14,9 @@ from ._binding import (  # noqa: F401
     attn_bwd,
     attn_decode,
     attn_decode_combine,
+    attn_decode_fused,
+    attn_decode_fused_paged,
+    attn_decode_fused_workspace,
     attn_decode_split,
     attn_decode_split_paged,
     attn_decode_workspace,
@@ -25,11 +28,13 @@ from ._binding import (  # noqa: F401
     decode,
     decode_auto,
     decode_buffers,
+    decode_fused,
     decode_paged,
     default_scale,
     fwd,
     fwd_local,
     fwd_qkvpacked,
     fwd_varlen,
+    fused_workspace,
     load_library,
 )

@@ -30,7 +30,8 @@ ERR_HIP = -6
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_fwd_qkvpacked", "attn_bwd",
            "attn_decode_split",
            "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
-           "attn_decode_workspace", "attn_status_str")
+           "attn_decode_workspace", "attn_decode_fused", "attn_decode_fused_paged",
+           "attn_decode_fused_workspace", "attn_status_str")
 
 _DTYPE_CODE = {torch.bfloat16: 0, torch.float16: 1}
 
@@ -64,6 +65,10 @@ def load_library() -> ctypes.CDLL:
         lib.attn_decode_split_paged.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, i, f,
                                                 i, p]
         lib.attn_decode_combine.argtypes = [p, p, p, p, p, i, i, i, i, i, i, p]
+        lib.attn_decode_fused.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, i, f, i, p]
+        lib.attn_decode_fused_paged.argtypes = [p, p, p, p, p, p, p, p, ll, i, i, i, i, i, i, i,
+                                                i, f, i, p]
+        lib.attn_decode_fused_workspace.argtypes = [i, i, i, i, i, i]
         lib.attn_status_str.argtypes = [i]
         lib.attn_fwd.restype = i
         lib.attn_fwd_varlen.restype = i
@@ -75,6 +80,9 @@ def load_library() -> ctypes.CDLL:
         lib.attn_decode_split.restype = i
         lib.attn_decode_split_paged.restype = i
         lib.attn_decode_combine.restype = i
+        lib.attn_decode_fused.restype = i
+        lib.attn_decode_fused_paged.restype = i
+        lib.attn_decode_fused_workspace.restype = ctypes.c_longlong
         lib.attn_status_str.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -410,4 +418,85 @@ def decode_auto(q, k_cache, v_cache, seq_lens, scale: float | None = None, strea
     o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     attn_decode(q, k_cache, v_cache, seq_lens, o, lse, workspace, scale, stream)
+    return o, lse
+
+
+def attn_decode_fused_workspace(B: int, Hq: int, Hkv: int, max_len: int, d: int,
+                                chunk: int) -> int:
+    """Floats of workspace attn_decode_fused needs; raises on a rejected shape."""
+    n = load_library().attn_decode_fused_workspace(B, Hq, Hkv, max_len, d, chunk)
+    if n < 0:
+        raise AttnError("attn_decode_fused_workspace", int(n))
+    return int(n)
+
+
+def fused_workspace(B: int, Hq: int, Hkv: int, max_len: int, d: int, chunk: int, device="cuda"):
+    """A zeroed workspace for attn_decode_fused (its counters must start at zero;
+    the kernel leaves them zero, so the tensor can be reused call after call)."""
+    n = attn_decode_fused_workspace(B, Hq, Hkv, max_len, d, chunk)
+    return torch.zeros((n,), dtype=torch.float32, device=device)
+
+
+def _check_workspace(workspace):
+    _need(workspace.dtype == torch.float32 and workspace.dim() == 1, "workspace: 1-D fp32")
+    _need(workspace.data_ptr() % 256 == 0, "workspace must be 256-byte aligned")
+
+
+def attn_decode_fused(q, k_cache, v_cache, seq_lens, o, lse, workspace, chunk: int,
+                      scale: float, stream=None) -> None:
+    """Calls attn_decode_fused. q [B,Hq,d], caches [B,Hkv,max_len,d], seq_lens [B] int32,
+    o [B,Hq,d], lse [B,Hq] fp32, workspace from fused_workspace()."""
+    _gpu(q, k_cache, v_cache, seq_lens, o, lse, workspace)
+    B, Hq, d = q.shape
+    _, Hkv, max_len, _ = k_cache.shape
+    _need(v_cache.shape == k_cache.shape and k_cache.shape[0] == B and k_cache.shape[3] == d,
+          "cache shapes")
+    _need(k_cache.dtype == q.dtype and v_cache.dtype == q.dtype and o.dtype == q.dtype,
+          "dtypes differ")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens [B] int32")
+    _need(tuple(o.shape) == (B, Hq, d), "o [B,Hq,d]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq), "lse [B,Hq] fp32")
+    _check_workspace(workspace)
+    st = load_library().attn_decode_fused(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens),
+                                          _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          B, Hq, Hkv, max_len, d, int(chunk), float(scale),
+                                          _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode_fused", st)
+
+
+def attn_decode_fused_paged(q, k_pages, v_pages, block_table, seq_lens, o, lse, workspace,
+                            chunk: int, scale: float, stream=None) -> None:
+    """Calls attn_decode_fused_paged (pages and block_table as attn_decode_split_paged)."""
+    _gpu(q, k_pages, v_pages, block_table, seq_lens, o, lse, workspace)
+    B, Hq, d = q.shape
+    num_pages, page_size, Hkv, _ = k_pages.shape
+    _need(v_pages.shape == k_pages.shape and k_pages.shape[3] == d, "page shapes")
+    _need(k_pages.dtype == q.dtype and v_pages.dtype == q.dtype and o.dtype == q.dtype,
+          "dtypes differ")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and
+          block_table.shape[0] == B, "block_table [B,max_pages] int32")
+    _need(seq_lens.dtype == torch.int32 and tuple(seq_lens.shape) == (B,), "seq_lens [B] int32")
+    _need(tuple(o.shape) == (B, Hq, d), "o [B,Hq,d]")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq), "lse [B,Hq] fp32")
+    _check_workspace(workspace)
+    st = load_library().attn_decode_fused_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(seq_lens), _ptr(o),
+        _ptr(lse), _ptr(workspace), workspace.numel(), B, Hq, Hkv, num_pages, page_size,
+        block_table.shape[1], d, int(chunk), float(scale), _dtype_code(q), _stream(stream))
+    if st != OK:
+        raise AttnError("attn_decode_fused_paged", st)
+
+
+def decode_fused(q, k_cache, v_cache, seq_lens, chunk: int = 512, scale: float | None = None,
+                 stream=None, workspace=None):
+    """Split-KV decode with the combine fused into one launch. Returns (o, lse)."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = fused_workspace(B, Hq, k_cache.shape[1], k_cache.shape[2], d, chunk, q.device)
+    o = torch.empty((B, Hq, d), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    attn_decode_fused(q, k_cache, v_cache, seq_lens, o, lse, workspace, chunk, scale, stream)
     return o, lse

@@ -242,6 +242,100 @@ extern "C" int attn_decode(const void* q, const void* k_cache, const void* v_cac
   return from_hip(mi355attn::launch_combine(c, s));
 }
 
+namespace {
+
+// Workspace of the fused decode, in 4-byte words: the counters [B, Hkv] (int32),
+// then part_lse [B, Hq, C], then part_o [B, Hq, C, d], each region starting on
+// a 256-byte boundary. Returns a negative status for a shape the fused decode
+// rejects.
+int64_t fused_layout(int B, int Hq, int Hkv, int max_len, int d, int chunk, int64_t* lse_off,
+                     int64_t* o_off) {
+  const int st = decode_shape_status(B, Hq, Hkv, max_len, d);
+  if (st != MI355ATTN_OK) return st;
+  if (chunk <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  const int64_t C = ((int64_t)max_len + chunk - 1) / chunk;
+  // One (sequence, kv-head) pair's partials are addressed with 32-bit byte
+  // offsets from its first partial.
+  if ((int64_t)(Hq / Hkv) * C * d * 4 >= ((int64_t)1 << 32)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (mi355attn::split_work_items(B, Hkv, max_len, chunk) > kMaxGrid ||
+      (int64_t)B * Hq * C > ((int64_t)1 << 40))
+    return MI355ATTN_ERR_BAD_SHAPE;
+  auto up = [](int64_t n) { return (n + 63) / 64 * 64; };
+  const int64_t l0 = up((int64_t)B * Hkv);
+  const int64_t o0 = l0 + up((int64_t)B * Hq * C);
+  if (lse_off) *lse_off = l0;
+  if (o_off) *o_off = o0;
+  return o0 + (int64_t)B * Hq * C * d;
+}
+
+int fused_args_status(const void* q, const void* k, const void* v, const int* seq_lens, void* o,
+                      float* lse, float* workspace, long long workspace_floats, int64_t need,
+                      float scale, int dtype) {
+  if (!q || !k || !v || !seq_lens || !o || !lse || !workspace) return MI355ATTN_ERR_NULL_PTR;
+  if (need < 0) return (int)need;
+  if (!dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
+  if (!scale_ok(scale)) return MI355ATTN_ERR_BAD_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(seq_lens, 4) || !aligned(workspace, 256))
+    return MI355ATTN_ERR_MISALIGNED;
+  if (workspace_floats < need) return MI355ATTN_ERR_BAD_ARG;
+  return MI355ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" long long attn_decode_fused_workspace(int B, int Hq, int Hkv, int max_len, int d,
+                                                 int chunk) {
+  return fused_layout(B, Hq, Hkv, max_len, d, chunk, nullptr, nullptr);
+}
+
+extern "C" int attn_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                                 const int* seq_lens, void* o, float* lse, float* workspace,
+                                 long long workspace_floats, int B, int Hq, int Hkv, int max_len,
+                                 int d, int chunk, float scale, int dtype, void* stream) {
+  int64_t l0 = 0, o0 = 0;
+  const int64_t need = fused_layout(B, Hq, Hkv, max_len, d, chunk, &l0, &o0);
+  const int st = fused_args_status(q, k_cache, v_cache, seq_lens, o, lse, workspace,
+                                   workspace_floats, need, scale, dtype);
+  if (st != MI355ATTN_OK) return st;
+  mi355attn::SplitArgs a{q, k_cache, v_cache, seq_lens, workspace + o0, workspace + l0, B, Hq,
+                         Hkv, max_len, d, chunk, scale, dtype};
+  a.o_final = o;
+  a.lse_final = lse;
+  a.counters = reinterpret_cast<int*>(workspace);
+  return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int attn_decode_fused_paged(const void* q, const void* k_pages, const void* v_pages,
+                                       const int* block_table, const int* seq_lens, void* o,
+                                       float* lse, float* workspace, long long workspace_floats,
+                                       int B, int Hq, int Hkv, int num_pages, int page_size,
+                                       int max_pages, int d, int chunk, float scale, int dtype,
+                                       void* stream) {
+  if (!block_table) return MI355ATTN_ERR_NULL_PTR;
+  if (num_pages <= 0 || page_size <= 0 || max_pages <= 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)max_pages * page_size > kMaxSeq || (int64_t)B * max_pages > kMaxGrid)
+    return MI355ATTN_ERR_BAD_SHAPE;
+  const int max_len = max_pages * page_size;
+  int64_t l0 = 0, o0 = 0;
+  const int64_t need = fused_layout(B, Hq, Hkv, max_len, d, chunk, &l0, &o0);
+  const int st = fused_args_status(q, k_pages, v_pages, seq_lens, o, lse, workspace,
+                                   workspace_floats, need, scale, dtype);
+  if (st != MI355ATTN_OK) return st;
+  const int item_pages = chunk % page_size == 0 ? chunk / page_size
+                                                : (chunk + page_size - 2) / page_size + 1;
+  if (page_size % 16 != 0 || chunk % 16 != 0 || item_pages > 16)
+    return MI355ATTN_ERR_UNSUPPORTED;
+  if (!aligned(block_table, 4)) return MI355ATTN_ERR_MISALIGNED;
+  mi355attn::SplitArgs a{q, k_pages, v_pages, seq_lens, workspace + o0, workspace + l0, B, Hq,
+                         Hkv, max_len, d, chunk, scale, dtype, block_table, page_size,
+                         max_pages, num_pages};
+  a.o_final = o;
+  a.lse_final = lse;
+  a.counters = reinterpret_cast<int*>(workspace);
+  return from_hip(mi355attn::launch_split(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_decode_combine(const float* part_o, const float* part_lse,
                                    const int* seq_lens, void* o, float* lse, int B, int Hq,
                                    int max_chunks, int d, int chunk, int dtype, void* stream) {

@@ -25,8 +25,8 @@
 // tile (plus the partial-result stores issued after it) means the tile has
 // landed. Because completion is in order, a store also holds back every load
 // issued after it until it is acknowledged; an item's output therefore waits
-// in registers and is stored one iteration later, right after that
-// iteration's wait, which gives the stores two tiles' time.
+// in registers and is stored one iteration later, after every load that
+// iteration issues, which gives the stores two tiles' time.
 //
 // Per tile: S^T[32 keys x 32 cols] = K Q^T (8 MFMAs 32x32x16), the running
 // max / sum update of the online softmax (the OnlineSoftmaxState of the
@@ -114,17 +114,37 @@ struct PagedKV {
   int page_size, max_pages, num_pages;
 };
 
+// Cache policy of the partial results in the fused form: device scope (sc1:
+// the store is complete only once it is visible to every XCD's L2, and the load
+// reads the value that is visible at device scope, not a line an XCD's L2 may
+// still hold) and streamed (nt).
+constexpr int kDeviceScopeNt = 18;  // sc1 | nt
+constexpr int kDeviceScope = 16;    // sc1
+
 // FINAL: every sequence fits one chunk (chunk >= max_len), so each item's
 // normalised output is the final one: it is written rounded to the input dtype
 // into o [B, Hq, d] and its LSE into lse [B, Hq], and no combine is needed
 // (sequences of length 0 get O = 0, LSE = -inf).
-template <int DT, int D, bool PAGED, bool FINAL>
+//
+// FUSED: the combine runs inside this kernel. Every (sequence, kv-head) pair
+// has a counter (caller's workspace, zero between calls). An item of a
+// sequence with more than one chunk stores its partial result with
+// device-scope stores; once those are known to be complete (counted waits,
+// two iterations later) the wave adds one to the pair's counter, and the wave
+// whose addition completes the count (the last of the pair's chunks to finish)
+// reads every partial of the pair back with device-scope loads, merges them
+// with the rescaling combine and writes o and lse, then sets the counter back
+// to zero. Nothing waits on another wave. A sequence of one chunk writes its
+// final output directly, as in FINAL.
+template <int DT, int D, bool PAGED, bool FINAL, bool FUSED>
 __global__ void __launch_bounds__(kSplitThreads, 1)
 attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc,
                          const uint16_t* __restrict__ vc, const int* __restrict__ seq_lens,
                          float* __restrict__ part_o, float* __restrict__ part_lse, int B, int Hq,
                          int Hkv, int max_len, int chunk, int C, float scale, PagedKV pk,
-                         uint16_t* __restrict__ o_fin, float* __restrict__ lse_fin) {
+                         uint16_t* __restrict__ o_fin, float* __restrict__ lse_fin,
+                         int* __restrict__ counters) {
+  static_assert(!(FINAL && FUSED), "one output mode");
   using Lay = SplitLayout<D>;
   constexpr int DS = D / 16;
   constexpr int DB = D / 32;
@@ -142,7 +162,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int gwave = blockIdx.x * kSplitWaves + wave;
   const int nwaves = gridDim.x * kSplitWaves;
 
-  if constexpr (FINAL) {
+  if constexpr (FINAL || FUSED) {
     // Empty sequences: O = 0, LSE = -inf (no item covers them).
     for (int64_t i = (int64_t)blockIdx.x * kSplitThreads + tid; i < (int64_t)B * Hq;
          i += (int64_t)gridDim.x * kSplitThreads) {
@@ -207,6 +227,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // A work position: item, tile inside the item, and the item's geometry.
   struct Pos {
     int item, tile, b, g, c, L, n_tiles;
+    int nc;                   // chunks of sequence b
     int lp0;                  // paged: first logical page of the chunk
     int pg[PAGED ? kMaxItemPages : 1];  // paged: physical pages of the chunk's pages
   };
@@ -225,6 +246,7 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     p.b = cb;
     p.c = idx - cbase;
     p.L = cl_len;
+    p.nc = cn;
     const int lo = p.c * chunk;
     const int hi = min(p.L, lo + chunk);
     p.n_tiles = (hi - lo + kSplitBN - 1) / kSplitBN;
@@ -313,36 +335,167 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   uint16_t* pend_fin = o_fin;
   float* pend_lse = FINAL ? lse_fin : part_lse;
   float pend_lse_val = 0.f;
+  // Fused form: whether the pending output is final (a one-chunk sequence),
+  // else its pair (sequence, kv-head), the sequence's chunk count and its chunk.
+  bool pend_final = FINAL;
+  int pend_b = 0, pend_g = 0, pend_nc = 0, pend_c = 0;
+  // Byte offsets, relative to the first partial of a pair, of this lane's head
+  // (column r32) in part_o and part_lse; a pair's partials span R*C*D*4 bytes
+  // (below 2^32, checked by the C ABI).
+  const uint32_t lane_po = (uint32_t)(r32 < R ? r32 : 0) * (uint32_t)C * (uint32_t)(D * 4);
+  const uint32_t lane_pl = (uint32_t)(r32 < R ? r32 : 0) * (uint32_t)C * 4u;
+  auto pair_rsrc_o = [&](int b, int g) {
+    return make_rsrc(part_o + ((int64_t)b * Hq + (int64_t)g * R) * C * D,
+                     (uint32_t)R * (uint32_t)C * (uint32_t)(D * 4));
+  };
+  auto pair_rsrc_l = [&](int b, int g) {
+    return make_rsrc(part_lse + ((int64_t)b * Hq + (int64_t)g * R) * C,
+                     (uint32_t)R * (uint32_t)C * 4u);
+  };
   // Exactly NS vector-memory stores (lanes 0 and 32 always take part).
   auto store_pending = [&]() {
     if (r32 < R) {
+      if (FINAL || (FUSED && pend_final)) {
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int d0 = db * 32 + 8 * gq + 4 * half;
-          if constexpr (FINAL) {
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = db * 32 + 8 * gq + 4 * half;
             *reinterpret_cast<u32x2_t*>(pend_fin + d0) =
                 (u32x2_t){pack2<DT>(opend[db][4 * gq + 0], opend[db][4 * gq + 1]),
                           pack2<DT>(opend[db][4 * gq + 2], opend[db][4 * gq + 3])};
-          } else {
+          }
+        if (half == 0) __builtin_nontemporal_store(pend_lse_val, pend_lse);
+      } else if constexpr (FUSED) {
+        const auto ro = pair_rsrc_o(pend_b, pend_g);
+        const auto rl = pair_rsrc_l(pend_b, pend_g);
+        const uint32_t cb = (uint32_t)pend_c * (uint32_t)(D * 4);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = db * 32 + 8 * gq + 4 * half;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, (f32x4_t){opend[db][4 * gq + 0], opend[db][4 * gq + 1],
+                                                      opend[db][4 * gq + 2], opend[db][4 * gq + 3]}),
+                ro, lane_po + cb + (uint32_t)d0 * 4u, 0, kDeviceScopeNt);
+          }
+        if (half == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pend_lse_val), rl,
+                                                lane_pl + (uint32_t)pend_c * 4u, 0, kDeviceScopeNt);
+      } else {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int d0 = db * 32 + 8 * gq + 4 * half;
             // The combine reads the partials once, later: stream them past
             // the caches instead of holding KV lines' space for them.
             __builtin_nontemporal_store((f32x4_t){opend[db][4 * gq + 0], opend[db][4 * gq + 1],
                                                   opend[db][4 * gq + 2], opend[db][4 * gq + 3]},
                                         reinterpret_cast<f32x4_t*>(pend_dst + d0));
           }
-        }
-      if (half == 0) __builtin_nontemporal_store(pend_lse_val, pend_lse);
+        if (half == 0) __builtin_nontemporal_store(pend_lse_val, pend_lse);
+      }
     }
     pend = false;
   };
 
+  // Fused form: the merge of pair (b, g) by the wave that completed its count.
+  // Lanes take (head r, 4 consecutive d values) pieces, 64 at a time; each
+  // reads the pair's nc chunk LSEs and partial outputs with device-scope loads
+  // (issued in batches, then used): M = max LSE_c, w_c = exp(LSE_c - M),
+  // O = sum w_c O_c / sum w_c (rounded to the dtype), LSE = M + log sum w_c
+  // (the two passes of the aprender-gpu reduce kernel; chunks with LSE = -inf
+  // carry no weight). Then the counter is set back to zero for the next call.
+  auto merge = [&](int b, int g, int nc) {
+    constexpr int CPH = D / 4;  // 16-byte pieces per head
+    constexpr int MB = 16;      // chunks per batch of loads
+    const auto ro = pair_rsrc_o(b, g);
+    const auto rl = pair_rsrc_l(b, g);
+    const int64_t row0 = (int64_t)b * Hq + (int64_t)g * R;
+    for (int p0 = 0; p0 < R * CPH; p0 += 64) {
+      const int pp = p0 + lane;
+      const bool on = pp < R * CPH;
+      const int r = on ? pp / CPH : 0;
+      const int c4 = pp % CPH;
+      const uint32_t vl = (uint32_t)r * (uint32_t)C * 4u;
+      const uint32_t vo = (uint32_t)r * (uint32_t)C * (uint32_t)(D * 4) + (uint32_t)c4 * 16u;
+      float M = -INFINITY;
+      for (int c0 = 0; c0 < nc; c0 += MB) {
+        float lc[MB];
+#pragma unroll
+        for (int u = 0; u < MB; ++u)
+          lc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rl, vl, min(c0 + u, nc - 1) * 4, kDeviceScope));
+#pragma unroll
+        for (int u = 0; u < MB; ++u) M = fmaxf(M, lc[u]);
+      }
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      float wsum = 0.f;
+      if (M != -INFINITY) {
+        for (int c0 = 0; c0 < nc; c0 += MB) {
+          float lc[MB];
+          f32x4_t x[MB];
+#pragma unroll
+          for (int u = 0; u < MB; ++u) {
+            const int c = min(c0 + u, nc - 1);
+            lc[u] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rl, vl, c * 4, kDeviceScope));
+            x[u] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, vo, c * (D * 4), kDeviceScope));
+          }
+#pragma unroll
+          for (int u = 0; u < MB; ++u) {
+            // chunks past nc (the batch's clamped repeats) and empty chunks: no weight
+            const float w = (c0 + u >= nc || lc[u] == -INFINITY)
+                                ? 0.f : fast_exp2((lc[u] - M) * kLog2e);
+            acc += w * x[u];
+            wsum += w;
+          }
+        }
+      }
+      if (on) {
+        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+        *reinterpret_cast<u32x2_t*>(o_fin + (row0 + r) * D + 4 * c4) =
+            (u32x2_t){pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
+        if (c4 == 0) lse_fin[row0 + r] = wsum > 0.f ? M + kLn2 * fast_log2(wsum) : -INFINITY;
+      }
+    }
+    if (lane == 0)
+      __hip_atomic_store(counters + (int64_t)b * Hkv + g, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // Fused form, pipeline of the counter additions. A pair's partials are
+  // stored last in iteration s; the wait of iteration s+2 finds them complete
+  // (every later wait leaves fewer operations in flight than were issued after
+  // them). At the top of iteration s+3, before that iteration's loads, the
+  // wave adds one to the pair's counter and waits for the old count (a full
+  // wait, but at a point where the only loads in flight are those of the tile
+  // it is about to use); the wave that completes the count merges. Slots: the
+  // pairs (b * Hkv + g, chunk count) stored one, two and three iterations ago.
+  bool s1 = false, s2 = false, s3 = false;
+  int s1_p = 0, s1_nc = 0, s2_p = 0, s2_nc = 0, s3_p = 0, s3_nc = 0;
+  auto count_top = [&]() {
+    if (s3) {
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(counters + s3_p, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+      if (__builtin_amdgcn_readfirstlane(old) == s3_nc - 1) merge(s3_p / Hkv, s3_p % Hkv, s3_nc);
+    }
+    s3 = s2, s3_p = s2_p, s3_nc = s2_nc;
+    s2 = s1, s2_p = s1_p, s2_nc = s1_nc;
+    s1 = false;
+  };
+
   while (have) {
+    if constexpr (FUSED) count_top();
     // The next position (next tile of this item, or the first tile of the
     // wave's next item) goes out before this tile's products. Then wait for
     // this tile (and, at an item's first tile, its Q rows): everything but the
-    // 2*NL loads just issued and the item-end stores issued before them.
+    // 2*NL loads just issued and the item-end stores the previous iteration
+    // issued last (after all of its loads).
     nxt = cur;
     bool have_next;
     if (cur.tile + 1 < cur.n_tiles) {
@@ -360,11 +513,6 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     } else {
       wait_all_memory();
     }
-    stores_out = false;
-    if (pend) {  // younger than the loads waited for above
-      store_pending();
-      stores_out = true;
-    }
     if (cur.tile == 0) {
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
@@ -374,6 +522,18 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       wait_lgkmcnt0();
     }
     if (have_next && nxt.tile == 0) issue_q(nxt);
+    // The previous item's output goes out last, after every load this
+    // iteration issues (the next tile and, when this tile is the last of its
+    // item, the next item's Q rows): the wait of the next iteration then only
+    // has to leave these NS stores and the 2*NL loads issued after them in
+    // flight, and everything older (the tile and the Q rows it will use) is
+    // known to have landed.
+    stores_out = false;
+    if (pend) {
+      if (FUSED && !pend_final) s1 = true, s1_p = pend_b * Hkv + pend_g, s1_nc = pend_nc;
+      store_pending();
+      stores_out = true;
+    }
 
     const unsigned char* kt = ring + stage * Lay::kStage;
     const unsigned char* vt = kt + Lay::kTile;
@@ -466,10 +626,14 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       const int64_t row = (int64_t)cur.b * Hq + (int64_t)cur.g * R + (r32 < R ? r32 : 0);
       const bool empty = !(l_row > 0.f);
       const float inv = empty ? 0.f : 1.f / lr_row;
-      if constexpr (FINAL) {
+      if constexpr (FUSED) {
+        pend_final = cur.nc == 1;
+        pend_b = cur.b, pend_g = cur.g, pend_nc = cur.nc, pend_c = cur.c;
+      }
+      if (FINAL || (FUSED && cur.nc == 1)) {
         pend_fin = o_fin + row * D;
         pend_lse = lse_fin + row;
-      } else {
+      } else if constexpr (!FUSED) {
         pend_dst = part_o + (row * C + cur.c) * D;
         pend_lse = part_lse + row * C + cur.c;
       }
@@ -491,7 +655,20 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     have = have_next;
     stage ^= 1;
   }
-  if (pend) store_pending();
+  if constexpr (FUSED) {
+    // Drain: once every store is complete, the remaining counter additions
+    // (each result waited for before it is used).
+    wait_all_memory();  // every partial store complete
+    for (int k = 0; k < 3; ++k) count_top();  // the pairs of slots s3, s2 and s1, in turn
+    if (pend) {  // the wave's last item (its slot is free now)
+      if (!pend_final) s1 = true, s1_p = pend_b * Hkv + pend_g, s1_nc = pend_nc;
+      store_pending();
+      wait_all_memory();
+      for (int k = 0; k < 3; ++k) count_top();
+    }
+  } else {
+    if (pend) store_pending();
+  }
 }
 
 template <int DT, int D>
@@ -609,25 +786,25 @@ static hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   const int C = (int)(((int64_t)max_len + a.chunk - 1) / a.chunk);
   const PagedKV pk{a.block_table, a.page_size, a.max_pages, a.num_pages};
   uint16_t* o_fin = (uint16_t*)a.o_final;
-  if (a.block_table) {
-    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, true, false>), dim3((unsigned)device_cus()),
-                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
-                       o_fin, a.lse_final);
+#define MI355_SPLIT_LAUNCH(P, FIN, FU)                                                           \
+  hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, P, FIN, FU>), dim3((unsigned)device_cus()), \
+                     dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,                       \
+                     (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,         \
+                     a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,   \
+                     o_fin, a.lse_final, a.counters)
+  if (a.counters) {
+    if (a.block_table)
+      MI355_SPLIT_LAUNCH(true, false, true);
+    else
+      MI355_SPLIT_LAUNCH(false, false, true);
+  } else if (a.block_table) {
+    MI355_SPLIT_LAUNCH(true, false, false);
   } else if (a.o_final) {
-    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false, true>), dim3((unsigned)device_cus()),
-                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
-                       o_fin, a.lse_final);
+    MI355_SPLIT_LAUNCH(false, true, false);
   } else {
-    hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, false, false>), dim3((unsigned)device_cus()),
-                       dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,
-                       (const uint16_t*)a.k_cache, (const uint16_t*)a.v_cache, a.seq_lens,
-                       a.part_o, a.part_lse, a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.scale, pk,
-                       o_fin, a.lse_final);
+    MI355_SPLIT_LAUNCH(false, false, false);
   }
+#undef MI355_SPLIT_LAUNCH
   return hipGetLastError();
 }
 

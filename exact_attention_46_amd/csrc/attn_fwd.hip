@@ -153,6 +153,16 @@ struct Window {
   int left, right;
 };
 
+// The 16-bit value at half `hi` of a dword, widened to fp32.
+template <int DT>
+__device__ __forceinline__ float widen16(uint32_t w, int hi) {
+  const uint32_t h = hi ? (w >> 16) : (w & 0xffffu);
+  if constexpr (DT == kBF16)
+    return __uint_as_float(h << 16);
+  else
+    return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+
 // VARLEN = false: dense [B, H, N, d] tensors of Nq / Nk rows per head.
 // VARLEN = true: packed batches (see VarLen); Nq / Nk are then the largest
 // sequence lengths, which size the grid, and each workgroup takes its
@@ -583,7 +593,68 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const float l_row = sum_with_partner32(l_part);
   const float lr_row = sum_with_partner32(lr_part);
   const bool empty = !(l_row > 0.f);
-  const float inv = empty ? 0.f : 1.f / lr_row;
+  float inv = empty ? 0.f : 1.f / lr_row;
+  if constexpr (CAUSAL || LOCAL) {
+    // A masked key has P = 0, but the products still form 0 * Inf or
+    // 0 * NaN = NaN from its V row in every row of the wave. A wave whose
+    // accumulators are all finite took no such value (and the common case
+    // ends here); otherwise its rows are recomputed key by key over each row's
+    // allowed keys only (Q from the wave's LDS block, K and V from memory,
+    // P = exp2(s * c - m) with the final offset m, fp32, into the same
+    // accumulators), so an Inf or NaN in V reaches exactly the rows that
+    // attend to its key. Only input holding Inf or NaN gets there.
+    bool fin = true;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        fin = fin && ((__float_as_uint(oacc[db][e]) & 0x7f800000u) != 0x7f800000u);
+    if (!__all(fin) && wave_rows_valid) {
+      int j_lo = 0, j_hi = Nk - 1;
+      if constexpr (CAUSAL) j_hi = min(Nk - 1, wave_last_row + off);
+      if constexpr (LOCAL) {
+        if (win.right >= 0) j_hi = min(Nk - 1, wave_last_row + off + win.right);
+        if (win.left >= 0) j_lo = max(0, qw0 + off - win.left);
+      }
+      const float neg_m = (m_used == -INFINITY) ? 0.f : -m_used;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] = (f32x16_t){};
+      const unsigned char* qrow = qslot + r32 * ROW;
+#pragma unroll 1
+      for (int j = j_lo; j <= j_hi; ++j) {
+        // this lane's half of q.k (d-chunks half*DS .. +DS-1), then its partner's
+        const uint16_t* kr = kh + (int64_t)j * KS + half * (D / 2);
+        float part = 0.f;
+#pragma unroll 2
+        for (int ds = 0; ds < DS; ++ds) {
+          const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(kr + 8 * ds);
+          const u32x4_t qq =
+              *reinterpret_cast<const u32x4_t*>(qrow + (((half * DS + ds) ^ kx) << 4));
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            part = __builtin_fmaf(widen16<DT>(qq[w], 0), widen16<DT>(kk[w], 0),
+                                  __builtin_fmaf(widen16<DT>(qq[w], 1), widen16<DT>(kk[w], 1), part));
+        }
+        const float sdot = sum_with_partner32(part);
+        bool allowed = my_row < Nq && j <= row_kmax;
+        if constexpr (LOCAL) allowed = allowed && j >= row_kmin;
+        if (allowed) {
+          const float p = fast_exp2(__builtin_fmaf(sdot, c, neg_m));
+          const uint16_t* vr = vh + (int64_t)j * KS + 4 * half;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const u32x2_t w2 = *reinterpret_cast<const u32x2_t*>(vr + 32 * db + 8 * gq);
+#pragma unroll
+              for (int cc = 0; cc < 4; ++cc)
+                oacc[db][4 * gq + cc] += p * widen16<DT>(w2[cc >> 1], cc & 1);
+            }
+        }
+      }
+      inv = empty ? 0.f : 1.f / l_row;  // these P were not rounded
+    }
+  }
   // O^T (lane: row r32, d = 32 db + 8 gq + 4 half + 0..3) goes row-major
   // through the wave's Q block in LDS (free since the prologue; 32 rows x ROW
   // bytes), 16-byte chunk c of row r stored at chunk c ^ (r mod chunks per

@@ -49,6 +49,10 @@ struct SplitArgs {
   // One pass (chunk >= max_len): final O [B, Hq, d] (dtype) and LSE [B, Hq].
   void* o_final = nullptr;
   float* lse_final = nullptr;
+  // Combine fused into the split kernel (counters != nullptr): one int32 per
+  // (sequence, kv-head) [B, Hkv], zero on entry and left zero; the partials go
+  // to part_o / part_lse and the final result to o_final / lse_final.
+  int* counters = nullptr;
 };
 
 struct CombineArgs {

@@ -279,6 +279,56 @@ int attn_decode(const void* q, const void* k_cache, const void* v_cache, const i
  */
 long long attn_decode_workspace(int B, int Hq, int Hkv, int max_len, int d);
 
+/*
+ * attn_decode_fused — split-KV decode in a single launch: the combine of the
+ * aprender-gpu "flash_decoding/reduce_kernel.rs" page (global maximum of the
+ * chunk LSEs, weights exp(LSE_c - M), weighted mean) runs inside the split
+ * kernel, started by the chunk that finishes last (a last-block-done counter
+ * per (sequence, kv-head) pair), so there is no second kernel and no pass over
+ * every partial by a separate launch. A sequence that fits one chunk writes
+ * its final output directly.
+ *
+ *   q, k_cache, v_cache, seq_lens  as attn_decode_split (chunk keys per chunk)
+ *   o          [B, Hq, d]   dtype  (written, rounded to nearest even)
+ *   lse        [B, Hq]      float  (written; a sequence of length 0 gets O = 0
+ *                                   and LSE = -inf)
+ *   workspace  attn_decode_fused_workspace(B, Hq, Hkv, max_len, d, chunk)
+ *              floats (workspace_floats given), 256-byte aligned, owned by the
+ *              caller: B*Hkv int32 counters first, then the chunk partials.
+ *              The counters must be zero the first time a workspace is used
+ *              (e.g. memory allocated zeroed); every call that runs to its end
+ *              leaves them zero again, so the workspace can be reused call
+ *              after call. Calls that overlap in time must not share one.
+ *
+ * The result equals attn_decode_split + attn_decode_combine with the same
+ * chunk (up to rounding). Needs (Hq/Hkv) * ceil(max_len/chunk) * d * 4 < 2^32
+ * (else MI355ATTN_ERR_UNSUPPORTED); a too-small workspace returns
+ * MI355ATTN_ERR_BAD_ARG.
+ */
+int attn_decode_fused(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse, float* workspace,
+                      long long workspace_floats, int B, int Hq, int Hkv, int max_len, int d,
+                      int chunk, float scale, int dtype, void* stream);
+
+/*
+ * attn_decode_fused_paged — attn_decode_fused over a paged KV cache; q,
+ * k_pages, v_pages, block_table, seq_lens, page_size and chunk as in
+ * attn_decode_split_paged (max_len = max_pages * page_size), o, lse and the
+ * workspace as in attn_decode_fused.
+ */
+int attn_decode_fused_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int* block_table, const int* seq_lens, void* o, float* lse,
+                            float* workspace, long long workspace_floats, int B, int Hq, int Hkv,
+                            int num_pages, int page_size, int max_pages, int d, int chunk,
+                            float scale, int dtype, void* stream);
+
+/*
+ * attn_decode_fused_workspace — floats of workspace attn_decode_fused (and
+ * attn_decode_fused_paged, with max_len = max_pages * page_size) needs for
+ * this shape and chunk, or a negative status code for a shape it rejects.
+ */
+long long attn_decode_fused_workspace(int B, int Hq, int Hkv, int max_len, int d, int chunk);
+
 /* A static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_str(int status);
 

@@ -208,6 +208,59 @@ def test_attn_decode_workspace_rejects_bad_shapes(lib):
     assert lib.attn_decode_workspace(2, 6, 4, 64, 128) == -2
 
 
+def fused(lib, q=A, kc=A, vc=A, sl=A2, o=A, lse=A2, ws=ctypes.c_void_p(1 << 20), wn=1 << 30,
+          B=2, Hq=8, Hkv=2, max_len=64, d=128, chunk=16, scale=0.1, dtype=0):
+    return lib.attn_decode_fused(q, kc, vc, sl, o, lse, ws, wn, B, Hq, Hkv, max_len, d, chunk,
+                                 scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(lse=None), -1), (dict(ws=None), -1),
+    (dict(B=0), -2), (dict(max_len=0), -2), (dict(chunk=0), -2), (dict(Hq=6, Hkv=4), -2),
+    (dict(max_len=2**23 + 1), -2),
+    (dict(d=80), -3), (dict(dtype=5), -3), (dict(Hq=66, Hkv=2), -3),
+    # one pair's partials span (Hq/Hkv) * C * d * 4 bytes, which must stay below 2^32
+    (dict(Hq=64, Hkv=2, max_len=2**23, chunk=16), -3),
+    (dict(scale=0.0), -5), (dict(kc=MIS), -4), (dict(ws=ctypes.c_void_p(4096 + 128)), -4),
+    (dict(wn=100), -5),
+])
+def test_attn_decode_fused_rejects(lib, kw, code):
+    assert fused(lib, **kw) == code
+
+
+def test_attn_decode_fused_workspace_layout(lib):
+    # counters [B*Hkv] and part_lse [B*Hq*C] each padded to 64 words, then part_o
+    up = lambda n: -(-n // 64) * 64
+    for B, Hq, Hkv, L, d, chunk in [(64, 32, 8, 32768, 128, 512), (3, 4, 1, 100, 64, 7),
+                                     (1, 1, 1, 1, 64, 1)]:
+        C = -(-L // chunk)
+        want = up(B * Hkv) + up(B * Hq * C) + B * Hq * C * d
+        assert lib.attn_decode_fused_workspace(B, Hq, Hkv, L, d, chunk) == want
+    assert lib.attn_decode_fused_workspace(0, 8, 2, 64, 128, 16) == -2
+    assert lib.attn_decode_fused_workspace(2, 8, 2, 64, 96, 16) == -3
+    assert lib.attn_decode_fused_workspace(2, 8, 2, 64, 128, 0) == -2
+
+
+def fused_paged(lib, q=A, kp=A, vp=A, bt=A2, sl=A2, o=A, lse=A2, ws=ctypes.c_void_p(1 << 20),
+                wn=1 << 30, B=2, Hq=8, Hkv=2, num_pages=10, page_size=32, max_pages=4, d=128,
+                chunk=64, scale=0.1, dtype=0):
+    return lib.attn_decode_fused_paged(q, kp, vp, bt, sl, o, lse, ws, wn, B, Hq, Hkv, num_pages,
+                                       page_size, max_pages, d, chunk, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(bt=None), -1), (dict(ws=None), -1),
+    (dict(B=0), -2), (dict(num_pages=0), -2), (dict(page_size=0), -2), (dict(max_pages=0), -2),
+    (dict(chunk=0), -2), (dict(max_pages=2**18, page_size=64), -2),
+    (dict(d=80), -3), (dict(page_size=24), -3), (dict(chunk=40), -3),
+    (dict(page_size=16, chunk=512), -3),
+    (dict(scale=float("nan")), -5), (dict(vp=MIS), -4), (dict(bt=ctypes.c_void_p(4098)), -4),
+    (dict(wn=10), -5),
+])
+def test_attn_decode_fused_paged_rejects(lib, kw, code):
+    assert fused_paged(lib, **kw) == code
+
+
 def combine(lib, po=A, pl=A2, sl=A2, o=A, lse=A2, B=2, Hq=8, C=4, d=128, chunk=16, dtype=0):
     return lib.attn_decode_combine(po, pl, sl, o, lse, B, Hq, C, d, chunk, dtype, None)
 

@@ -134,16 +134,21 @@ def test_fwd_edge_shapes(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     check(o, lse, ro, rl, dtype, "edge %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, causal),))
 
 
-def test_fwd_score_outliers_exercise_rescale():
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_fwd_score_outliers_exercise_rescale(dtype):
     # 1% of key rows x10 (the long-context stress pattern) at a size the oracle
-    # finishes whole: rows jump in max many times.
+    # finishes whole: rows jump in max many times. Rows are then nearly one-hot
+    # and |O| exceeds 4, where bf16 rounding alone exceeds 1e-2, so the bf16 run
+    # is judged on the excess over that rounding; the fp16 run (half an ulp is
+    # 2^-9 there) takes the plain 4e-3 gate.
     B, H, N, d = 1, 4, 2048, 128
-    q, k, v = wl.prefill_inputs(B, H, H, N, N, d, "bf16", 44, outlier_frac=0.01,
+    q, k, v = wl.prefill_inputs(B, H, H, N, N, d, dtype, 44, outlier_frac=0.01,
                                 outlier_scale=10.0)
     scale = 1.0 / math.sqrt(d)
     o, lse = run_fwd(*_dev(q, k, v), True, scale)
-    ro, rl = oracle.attn_fwd(wl.bits(q), wl.bits(k), wl.bits(v), 0, scale, True)
-    check(o, lse, ro, rl, "bf16", "outliers", floor_aware=True)
+    ro, rl = oracle.attn_fwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.DTYPE_CODE[dtype], scale,
+                             True)
+    check(o, lse, ro, rl, dtype, "outliers", floor_aware=(dtype == "bf16"))
 
 
 def test_fwd_nan_only_poisons_rows_that_see_it():
@@ -157,9 +162,66 @@ def test_fwd_nan_only_poisons_rows_that_see_it():
     assert torch.isfinite(o[0, 1]).all()
 
 
+# Non-finite inputs (a NaN or Inf must reach exactly the rows that attend to its
+# key). Plants: (tensor, batch, head, key row, column, value); keys placed in
+# tiles the causal or window limits cut through, so some rows of the same tile
+# must not see them.
+NONFINITE = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype, mask (True causal, False none, (left, right)), plants
+    (1, 4, 2, 300, 300, 128, "bf16", True,
+     [("v", 0, 0, 150, 3, "nan"), ("v", 0, 0, 170, 5, "inf"), ("v", 0, 1, 10, 0, "-inf"),
+      ("k", 0, 1, 200, 7, "nan"), ("v", 0, 1, 40, 9, "inf")]),
+    (1, 2, 2, 200, 300, 64, "fp16", True,
+     [("v", 0, 0, 250, 1, "inf"), ("k", 0, 1, 180, 2, "inf"), ("v", 0, 1, 299, 0, "nan")]),
+    (1, 2, 2, 300, 300, 128, "bf16", False,
+     [("v", 0, 0, 77, 4, "nan"), ("k", 0, 1, 130, 0, "nan")]),
+    (1, 2, 2, 300, 300, 128, "bf16", (50, 0),
+     [("v", 0, 0, 100, 6, "nan"), ("v", 0, 1, 260, 2, "-inf"), ("k", 0, 1, 40, 1, "nan")]),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,mask,plants", NONFINITE)
+def test_fwd_nonfinite_reaches_only_attending_rows(B, Hq, Hkv, Nq, Nk, d, dtype, mask, plants):
+    seed = zlib.crc32(repr(("nonfinite", B, Hq, Hkv, Nq, Nk, d, dtype)).encode()) % 10000
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed)
+    for name, b, h, j, c, val in plants:
+        {"k": k, "v": v}[name][b, h, j, c] = float(val)
+    scale = 1.0 / math.sqrt(d)
+    dc = wl.DTYPE_CODE[dtype]
+    qd, kd, vd = _dev(q, k, v)
+    if isinstance(mask, tuple):
+        o = torch.empty_like(qd)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+        ea.attn_fwd_local(qd, kd, vd, o, lse, mask[0], mask[1], scale)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attn_fwd_local(wl.bits(q), wl.bits(k), wl.bits(v), dc, scale, *mask)
+    else:
+        o, lse = run_fwd(qd, kd, vd, mask, scale)
+        ro, rl = oracle.attn_fwd(wl.bits(q), wl.bits(k), wl.bits(v), dc, scale, mask)
+    og = o.float().cpu().double().numpy()
+    lg = lse.cpu().double().numpy()
+    what = "non-finite %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, mask),)
+    # the same elements are NaN, +Inf and -Inf as in the oracle's exact result
+    for f in (np.isnan, np.isposinf, np.isneginf):
+        bad = np.argwhere(f(og) != f(ro))
+        assert bad.size == 0, "%s: %s differs at %d elements, first %s (gpu %r, oracle %r)" % (
+            what, f.__name__, len(bad), tuple(bad[0]), og[tuple(bad[0])], ro[tuple(bad[0])])
+    assert np.array_equal(np.isnan(lg), np.isnan(rl)), what + ": NaN LSE pattern"
+    assert np.array_equal(np.isneginf(lg), np.isneginf(rl)), what + ": -inf LSE pattern"
+    assert (~np.isfinite(ro)).any(), what + ": nothing planted reached an output"
+    fin = np.isfinite(ro)
+    assert fin.any(), what + ": no finite output left to compare"
+    assert np.abs(og[fin] - ro[fin]).max() <= TOL_O[dtype], what + ": finite O"
+    lfin = np.isfinite(rl)
+    if lfin.any():
+        assert np.abs(lg[lfin] - rl[lfin]).max() <= TOL_LSE, what + ": finite LSE"
+
+
 # --------------------------------------------------------------- prefill, full size
 
-def _sample_rows(B, H, N, per_unit, seed, extra=()):
+def _sample_rows(B, H, N, per_unit, seed, extra=(), extra_per_head=None):
+    """Seeded rows per (b, h): `per_unit` drawn without replacement, plus `extra`
+    (every unit) and `extra_per_head(b, h)` (that unit)."""
     rng = np.random.default_rng(seed)
     rows = []
     for b in range(B):
@@ -167,38 +229,60 @@ def _sample_rows(B, H, N, per_unit, seed, extra=()):
             picks = set(rng.choice(N, size=min(per_unit, N), replace=False).tolist())
             picks.update([0, N - 1])
             picks.update(extra)
+            if extra_per_head is not None:
+                picks.update(extra_per_head(b, h))
             rows += [(b, h, i) for i in sorted(picks) if 0 <= i < N]
     return np.array(rows, dtype=np.int64)
 
 
-def _full_size(name, per_unit, floor_aware=False, extra_rows=None):
+def _full_size(name, rows_of, floor_aware=False):
     w = wl.WORKLOADS[name]
     q, k, v = wl.workload_prefill_inputs(w)
     o, lse = run_fwd(*_dev(q, k, v), True, w.scale)
     # whole-tensor properties
     assert torch.isfinite(o).all()
     assert torch.isfinite(lse).all()
-    rows = _sample_rows(w.B, w.Hq, w.N, per_unit, w.seed, extra_rows or ())
+    rows = rows_of(w)
     ro, rl = oracle.attn_fwd_rows(wl.bits(q), wl.bits(k), wl.bits(v), 0, w.scale, True, rows)
     idx = torch.from_numpy(rows)
     og = o.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
     lg = lse.cpu()[idx[:, 0], idx[:, 1], idx[:, 2]]
+    print("%s: %d rows compared" % (name, len(rows)))
     return check(og, lg, ro, rl, w.dtype, name, floor_aware=floor_aware)
 
 
-def test_llm_prefill_full_size_sampled():
-    _full_size("llm_prefill", per_unit=12)
+def _edges(N):
+    return list(range(64)) + list(range(N - 64, N))
+
+
+def test_llm_prefill_full_size_every_row():
+    """The whole llm_prefill workload (B=4, H=32, N=2048) in the launch the
+    benchmark times, every one of its 262 144 rows against the oracle."""
+    w = wl.WORKLOADS["llm_prefill"]
+    q, k, v = wl.workload_prefill_inputs(w)
+    o, lse = run_fwd(*_dev(q, k, v), True, w.scale)
+    ro, rl = oracle.attn_fwd(wl.bits(q), wl.bits(k), wl.bits(v), 0, w.scale, True)
+    check(o, lse, ro, rl, w.dtype, "llm_prefill, every row")
 
 
 def test_gqa_prefill_full_size_sampled():
-    _full_size("gqa_prefill", per_unit=10)
+    """256 seeded rows of every (b, h) plus its first and last 64 rows."""
+    _full_size("gqa_prefill",
+               lambda w: _sample_rows(w.B, w.Hq, w.N, 256, w.seed, extra=_edges(w.N)))
 
 
 def test_long_context_full_size_sampled():
+    """256 seeded rows of every head plus its first and last 64 rows, plus every
+    query row at the index of one of the head's outlier (x10) keys; the gate is
+    on the excess over the bf16 rounding of the exact result (outputs reach
+    |O| > 4 there, where that rounding alone exceeds 1e-2)."""
     w = wl.WORKLOADS["long_context"]
     outl = wl.outlier_rows(w.B, w.Hq, w.Hkv, w.N, w.N, w.d, w.seed, w.outlier_frac)
-    extra = sorted(set(outl[0][0][:4] + outl[0][1][:4]))
-    _full_size("long_context", per_unit=6, floor_aware=True, extra_rows=extra)
+    group = w.Hq // w.Hkv
+    _full_size("long_context",
+               lambda w: _sample_rows(w.B, w.Hq, w.N, 256, w.seed, extra=_edges(w.N),
+                                      extra_per_head=lambda b, h: outl[b][h // group]),
+               floor_aware=True)
 
 
 # --------------------------------------------------------------- decode
@@ -211,6 +295,12 @@ DECODE = [
     (2, 32, 1, 128, "bf16", [1500, 333], 1536, 100),
     (6, 16, 2, 64, "bf16", [5, 40, 77, 128, 129, 3], 130, 7),
     (2, 8, 8, 128, "fp16", [4096, 4000], 4096, 4096),
+    # 16 384 / 12 288 items for 1 024 waves: every wave walks many items that are
+    # a single 32-key tile (chunk 32) or one tile and a 16-key tail (chunk 48),
+    # so an item's Q rows are fetched right after the previous item's stores
+    (64, 32, 8, 128, "bf16", None, 1024, 32),
+    (64, 32, 8, 128, "bf16", None, 1024, 48),
+    (64, 16, 8, 64, "fp16", None, 1024, 32),
 ]
 
 
@@ -267,22 +357,150 @@ def test_decode_combine_alone_with_empty_chunks():
     assert (o[1].float() == 0).all()
 
 
-def test_decode_full_size_sampled():
+def test_decode_full_size_every_sequence():
+    """The decode workload (64 sequences, L ~ U[512, 32768], 512-key chunks) in
+    the launches the benchmark times: every valid chunk partial of every
+    sequence against the oracle's chunk partials, and every final output
+    against the oracle's direct decode."""
     w = wl.WORKLOADS["decode"]
     sl, q, kc, vc = wl.workload_decode_inputs(w, device="cuda")
     qd, sld = q.cuda(), sl.cuda()
-    o, lse = ea.decode(qd, kc, vc, sld, chunk=w.chunk, scale=w.scale)
+    C = -(-w.l_max // w.chunk)
+    pob, po = _guarded((w.B, w.Hq, C, w.d), torch.float32)
+    plb, pl = _guarded((w.B, w.Hq, C), torch.float32)
+    ob, o = _guarded((w.B, w.Hq, w.d), torch.bfloat16)
+    lb, lse = _guarded((w.B, w.Hq), torch.float32)
+    ea.attn_decode_split(qd, kc, vc, sld, po, pl, w.chunk, w.scale)
+    ea.attn_decode_combine(po, pl, sld, o, lse, w.chunk)
     torch.cuda.synchronize()
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    for buf, t in ((pob, po), (plb, pl), (ob, o), (lb, lse)):
+        assert _guard_ok(buf, t.numel()), "write outside an output"
+    kb, vb = wl.bits(kc), wl.bits(vc)  # rows past each length are NaN and never read
     lens = sl.numpy()
-    picks = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 0, 17, 42, 63})
-    for b in picks:
-        L = int(lens[b])
-        kb = kc[b:b + 1, :, :L].cpu()
-        vb = vc[b:b + 1, :, :L].cpu()
-        ro, rl = oracle.decode(wl.bits(q[b:b + 1]), wl.bits(kb), wl.bits(vb),
-                               np.array([L], dtype=np.int32), 0, w.scale)
-        check(o[b:b + 1], lse[b:b + 1], ro, rl, "bf16", "decode seq %d (L=%d)" % (b, L))
+    rpo, rpl = oracle.decode_chunks(wl.bits(q), kb, vb, lens, 0, w.chunk, w.scale)
+    pl_h = pl.cpu().double().numpy()
+    assert np.array_equal(np.isneginf(pl_h), np.isneginf(rpl))
+    valid = np.isfinite(rpl)
+    assert valid.sum() == w.Hq * int(sum(-(-int(L) // w.chunk) for L in lens))
+    po_h = po.cpu().double().numpy()
+    assert np.isfinite(po_h[valid]).all()
+    perr = np.abs(po_h[valid] - rpo[valid]).max()
+    assert perr <= TOL_O["bf16"], "partials: O max err %.3e" % perr
+    assert np.abs(pl_h[valid] - rpl[valid]).max() <= TOL_LSE
+    ro, rl = oracle.decode(wl.bits(q), kb, vb, lens, 0, w.scale)
+    check(o, lse, ro, rl, "bf16", "decode, every sequence")
+
+
+# --------------------------------------------------------------- decode, combine fused
+
+FUSED = [
+    # B, Hq, Hkv, d, dtype, lens, max_len, chunk
+    (5, 8, 2, 128, "bf16", [1, 9, 0, 31, 16], 32, 16),        # empty and one-chunk sequences
+    (4, 32, 8, 128, "bf16", None, 2048, 512),
+    (3, 4, 4, 64, "fp16", [700, 1, 513], 1024, 64),
+    (2, 32, 1, 128, "bf16", [1500, 333], 1536, 100),          # 32 heads per kv-head, ragged chunks
+    (6, 16, 2, 64, "bf16", [5, 40, 77, 128, 129, 3], 130, 7),
+    (64, 32, 8, 128, "bf16", None, 1024, 32),                 # many one-tile items per wave
+    (16, 8, 8, 128, "bf16", None, 4096, 64),                  # up to 64 chunks per pair
+    (2, 8, 8, 128, "fp16", [4096, 4000], 4096, 4096),         # every sequence one chunk
+]
+
+
+def _fused_call(q, kc, vc, sl, ws, chunk, scale):
+    B, Hq, d = q.shape
+    ob, o = _guarded((B, Hq, d), q.dtype)
+    lb, lse = _guarded((B, Hq), torch.float32)
+    ea.attn_decode_fused(q, kc, vc, sl, o, lse, ws, chunk, scale)
+    torch.cuda.synchronize()
+    assert _guard_ok(ob, o.numel()) and _guard_ok(lb, lse.numel()), "write outside an output"
+    return o, lse
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dtype,lens,max_len,chunk", FUSED)
+def test_decode_fused(B, Hq, Hkv, d, dtype, lens, max_len, chunk):
+    """The combine fused into the split kernel (last chunk of each (sequence,
+    kv-head) merges): against the oracle's direct decode and against the
+    two-kernel split + combine at the same chunk, twice on one workspace (the
+    kernel resets its counters), the second call on other lengths."""
+    seed = 4000 + B * 7 + Hq + d + chunk
+    sl, q, kc, vc = wl.decode_inputs(B, Hq, Hkv, d, dtype, seed, l_min=1, l_max=max_len,
+                                     max_len=max_len, device="cpu", seq_lens=lens)
+    scale = 1.0 / math.sqrt(d)
+    dc = wl.DTYPE_CODE[dtype]
+    qd, kcd, vcd, sld = _dev(q, kc, vc, sl)
+    n = ea.attn_decode_fused_workspace(B, Hq, Hkv, max_len, d, chunk)
+    wsb, ws = _guarded((n,), torch.float32)  # the guard band keeps 256-byte alignment
+    ws.zero_()
+    for call in range(2):
+        if call == 1:  # shorter lengths (rows past the first lengths are NaN), one empty
+            g = torch.Generator().manual_seed(seed + 1)
+            sl = torch.minimum(torch.randint(0, max_len + 1, (B,), generator=g,
+                                             dtype=torch.int32), sl)
+            sl[0] = 0
+            sld = sl.cuda()
+        o, lse = _fused_call(qd, kcd, vcd, sld, ws, chunk, scale)
+        counters = ws[:B * Hkv].view(torch.int32).cpu()
+        assert (counters == 0).all(), "counters not reset: %s" % counters[counters != 0][:8]
+        ro, rl = oracle.decode(wl.bits(q), wl.bits(kc), wl.bits(vc), sl.numpy(), dc, scale)
+        check(o, lse, ro, rl, dtype, "fused decode, call %d" % call,
+              floor_aware=max_len <= 64)
+        # against the two-kernel path at the same chunk
+        o2, l2 = ea.decode(qd, kcd, vcd, sld, chunk=chunk, scale=scale)
+        torch.cuda.synchronize()
+        assert torch.equal(torch.isneginf(lse), torch.isneginf(l2))
+        fin = torch.isfinite(l2)
+        assert (lse[fin] - l2[fin]).abs().max().item() <= 1e-5
+        assert (o.float() - o2.float()).abs().max().item() <= TOL_O[dtype] / 2
+    assert _guard_ok(wsb, ws.numel()), "write outside the workspace"
+
+
+def test_decode_fused_full_size_every_sequence():
+    """The fused decode on the whole decode workload (64 sequences, 512-key
+    chunks, up to 64 chunks per pair): every sequence against the oracle."""
+    w = wl.WORKLOADS["decode"]
+    sl, q, kc, vc = wl.workload_decode_inputs(w, device="cuda")
+    qd, sld = q.cuda(), sl.cuda()
+    ws = ea.fused_workspace(w.B, w.Hq, w.Hkv, w.l_max, w.d, w.chunk)
+    for call in range(2):  # the second call reuses the workspace the first reset
+        o, lse = ea.decode_fused(qd, kc, vc, sld, chunk=w.chunk, scale=w.scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert (ws[:w.B * w.Hkv].view(torch.int32) == 0).all()
+    ro, rl = oracle.decode(wl.bits(q), wl.bits(kc), wl.bits(vc), sl.numpy(), 0, w.scale)
+    check(o, lse, ro, rl, "bf16", "fused decode, every sequence")
+    # the paged cache through the fused path: bit-identical to the contiguous one
+    kp, vp, table = wl.paged_from_padded(kc, vc, sl, 64, seed=w.seed)
+    o_p = torch.empty_like(o)
+    l_p = torch.empty_like(lse)
+    ea.attn_decode_fused_paged(qd, kp, vp, table.cuda(), sld, o_p, l_p, ws, w.chunk, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o_p.view(torch.int16), o.view(torch.int16))
+    assert torch.equal(l_p, lse)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,d,dtype,lens,max_len,page_size,chunk", [
+    (5, 8, 2, 128, "bf16", [1, 9, 0, 31, 16], 32, 16, 32),
+    (3, 4, 4, 64, "fp16", [700, 1, 513], 1024, 64, 64),
+    (6, 16, 2, 64, "bf16", [5, 40, 77, 128, 129, 3], 160, 32, 48),
+    (64, 32, 8, 128, "bf16", None, 1024, 32, 32),
+])
+def test_paged_decode_fused(B, Hq, Hkv, d, dtype, lens, max_len, page_size, chunk):
+    seed = 5000 + B * 7 + Hq + d + page_size
+    sl, q, kc, vc = wl.decode_inputs(B, Hq, Hkv, d, dtype, seed, l_min=1, l_max=max_len,
+                                     max_len=max_len, device="cpu", seq_lens=lens)
+    kp, vp, table = wl.paged_from_padded(kc, vc, sl, page_size, seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    qd, kpd, vpd, td, sld = _dev(q, kp, vp, table, sl)
+    max_pages = table.shape[1]
+    ws = ea.fused_workspace(B, Hq, Hkv, max_pages * page_size, d, chunk)
+    ob, o = _guarded((B, Hq, d), q.dtype)
+    lb, lse = _guarded((B, Hq), torch.float32)
+    ea.attn_decode_fused_paged(qd, kpd, vpd, td, sld, o, lse, ws, chunk, scale)
+    torch.cuda.synchronize()
+    assert _guard_ok(ob, o.numel()) and _guard_ok(lb, lse.numel()), "write outside an output"
+    assert (ws[:B * Hkv].view(torch.int32) == 0).all()
+    ro, rl = oracle.decode_paged(wl.bits(q), wl.bits(kp), wl.bits(vp), table.numpy(),
+                                 sl.numpy(), wl.DTYPE_CODE[dtype], scale)
+    check(o, lse, ro, rl, dtype, "paged fused decode", floor_aware=max_len <= 64)
 
 
 # --------------------------------------------------------------- paged decode
@@ -296,6 +514,8 @@ PAGED = [
     (6, 16, 2, 64, "bf16", [5, 40, 77, 128, 129, 3], 160, 32, 48),
     (3, 8, 2, 128, "bf16", [700, 256, 17], 768, 16, 256),
     (2, 8, 8, 128, "fp16", [4096, 4000], 4096, 512, 4096),
+    # many single-tile items per wave (see DECODE)
+    (64, 32, 8, 128, "bf16", None, 1024, 32, 32),
 ]
 
 
@@ -506,6 +726,10 @@ AUTO = [
     (64, 32, 8, 128, "bf16", None, 512),         # split into 256-key chunks + combine
     (300, 8, 8, 64, "fp16", [0, 1, 300] * 100, 300),  # one pass, empty sequences included
     (16, 32, 8, 128, "bf16", None, 2048),
+    # one pass, 8 192 items of one 32-key tile each: every wave walks eight of them
+    (1024, 32, 8, 128, "bf16", None, 32),
+    # one pass, items of one or two tiles, four per wave
+    (512, 8, 8, 128, "bf16", None, 64),
 ]
 
 
@@ -526,7 +750,10 @@ def test_decode_one_call(B, Hq, Hkv, d, dtype, lens, max_len):
         assert _guard_ok(buf, t.numel()), "write outside an output or the workspace"
     ro, rl = oracle.decode(wl.bits(q), wl.bits(kc), wl.bits(vc), sl.numpy(), wl.DTYPE_CODE[dtype],
                            scale)
-    check(o, lse, ro, rl, dtype, "one-call decode (workspace %d floats)" % n)
+    # Sequences of at most 64 keys give outputs close to single V rows (|O| up
+    # to about 4.5), where bf16 rounding alone exceeds the gate: judge the excess.
+    check(o, lse, ro, rl, dtype, "one-call decode (workspace %d floats)" % n,
+          floor_aware=max_len <= 64)
 
 
 def test_decode_one_call_workspace_sizes():
