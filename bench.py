@@ -19,9 +19,17 @@ Prints ONE JSON line:
   decode_auto   the same decode through attn_decode (the library's chunk length)
   decode_paged  the same decode over a paged cache (64-row pages, shuffled pool,
                 block tables), timed in a loop of its own after the steps
+  decode_fused  the same decode (512-key chunks) with the combine fused into the
+                split kernel (attn_decode_fused), one launch per decode
+  decode_fused_paged  the same over the paged cache (attn_decode_fused_paged)
+  fwd_tiny      the tiny fp16 workload (B=1 H=2 N=128 d=64), causal and not,
+                microseconds per call (launch-bound; no roofline claim)
   roofline    the forward kernel against the bf16 dense MFMA peak
-  cpu_baseline  the fp64 CPU oracle timed on a bounded row sample of the prefill
-                workload, in the same TFLOP/s unit
+  cpu_baseline  the fp64 CPU oracle on every row of the prefill workload, in the
+                same TFLOP/s unit, plus the tiny workload in full, seeded row
+                subsets of the GQA-prefill and long-context workloads (with the
+                full-workload time extrapolated from the subset's share of the
+                work) and the whole decode workload in KV GB/s
 """
 from __future__ import annotations
 
@@ -65,11 +73,14 @@ def parse():
     ap.add_argument("--no-auto", action="store_true",
                     help="skip the one-call decode (library chunk) measurement")
     ap.add_argument("--no-paged", action="store_true",
-                    help="skip the paged-cache decode measurement")
+                    help="skip the paged-cache decode measurements")
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused-combine decode measurements")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the forward on the GQA-prefill and long-context workloads")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
-                    help="restrict the timed step (for per-kernel profiles)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"] + ONLY_EXTRA, default="all",
+                    help="restrict the timed step (for per-kernel profiles); the extra choices "
+                         "run only that measurement, --steps times after --warmup untimed runs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain streaming kernel of known size "
                          "(the calibration of HBM byte counters)")
@@ -78,6 +89,11 @@ def parse():
                          "'bench.py --copy-calibration' into " + TRAFFIC_FILE)
     return ap.parse_args()
 
+
+# Single measurements for counter runs (bench.py --only NAME): the forward on
+# another workload, the backward, the fused decode and its paged form.
+ONLY_EXTRA = ["fwd_gqa_prefill", "fwd_long_context", "bwd", "decode_fused", "decode_fused_paged",
+              "fwd_local"]
 
 COPY_CAL_BYTES = 256 << 20  # bytes read (and written) by one calibration launch
 COPY_CAL_MATCH = "neg"      # the calibration kernel's name contains this
@@ -166,48 +182,89 @@ def load_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def _rows_flops(rows, N, d):
+    """Metric flops of causal rows (row i attends i + 1 keys)."""
+    import numpy as np
+    return float(np.sum(4.0 * (rows[:, 2] + 1) * d))
+
+
 def cpu_baseline(w, q, k, v, target_s):
-    """Times the fp64 oracle on a seeded sample of query rows of the prefill workload."""
+    """The fp64 oracle as it stands on the host's cores: every row of the prefill
+    workload (its whole fp64 forward), and a seeded row sample of it on one thread."""
     import numpy as np
 
     import oracle
     from exact_attention_46_amd import workloads as wl
 
     qb, kb, vb = wl.bits(q), wl.bits(k), wl.bits(v)
-    rng = np.random.default_rng(12345)
     cores = oracle.max_threads()  # the oracle keeps the last thread count it was given
-
-    def sample(n):
-        b = rng.integers(0, w.B, n)
-        h = rng.integers(0, w.Hq, n)
-        i = rng.integers(0, w.N, n)
-        return np.stack([b, h, i], axis=1).astype(np.int64)
-
-    def run(rows):
-        t0 = time.perf_counter()
-        oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows, nthreads=cores)
-        dt = time.perf_counter() - t0
-        flops = float(np.sum(4.0 * (rows[:, 2] + 1) * w.d))  # metric convention, causal
-        return dt, flops
-
-    dt, fl = run(sample(256))
-    n = int(min(2_000_000, max(256, 256 * target_s / max(dt, 1e-3))))
-    rows = sample(n)
-    dt, fl = run(rows)
-    # the same oracle on one thread, on a sample of about a tenth of the time
-    rows1 = rows[: max(16, n // (10 * max(1, cores)))]
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qb, kb, vb, 0, w.scale, True, nthreads=cores)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * w.B * w.Hq * w.N * w.N * w.d / 2.0  # the metric's causal convention
+    # one thread, on seeded random rows worth about a tenth of target_s
+    rng = np.random.default_rng(12345)
+    n1 = int(max(64, w.B * w.Hq * w.N * min(1.0, 0.1 * target_s / max(dt * cores, 1e-3))))
+    rows1 = np.stack([rng.integers(0, w.B, n1), rng.integers(0, w.Hq, n1),
+                      rng.integers(0, w.N, n1)], axis=1).astype(np.int64)
     t0 = time.perf_counter()
     oracle.attn_fwd_rows(qb, kb, vb, 0, w.scale, True, rows1, nthreads=1)
     dt1 = time.perf_counter() - t0
-    fl1 = float(np.sum(4.0 * (rows1[:, 2] + 1) * w.d))
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
-            "sample": "%d seeded random query rows of the llm_prefill workload (exact fp64 "
-                      "causal rows, avg %d keys), %.1f s" % (n, int(rows[:, 2].mean()) + 1, dt),
+            "sample": "all %d rows of the llm_prefill workload, each once (its whole exact "
+                      "fp64 causal forward), %.2f s" % (w.B * w.Hq * w.N, dt),
             "seconds": dt,
-            "one_thread": {"value": fl1 / dt1 / 1e12, "unit": "TFLOP/s",
-                           "sample": "the first %d of those rows, %.1f s" % (len(rows1), dt1)},
+            "one_thread": {"value": _rows_flops(rows1, w.N, w.d) / dt1 / 1e12,
+                           "unit": "TFLOP/s",
+                           "sample": "%d seeded random rows of the same workload on one "
+                                     "thread, %.2f s" % (n1, dt1)},
             "host": {"nproc": os.cpu_count(), "cpu_model": _cpu_model()}}
+
+
+def cpu_baseline_tiny(cores):
+    """The oracle on the whole tiny fp16 workload, both masks."""
+    import oracle
+    from exact_attention_46_amd import workloads as wl
+
+    w = wl.WORKLOADS["tiny"]
+    q, k, v = (wl.bits(t) for t in wl.workload_prefill_inputs(w))
+    out = {}
+    for causal in (False, True):
+        reps = 20
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle.attn_fwd(q, k, v, 1, w.scale, causal, nthreads=cores)
+        dt = (time.perf_counter() - t0) / reps
+        out["causal" if causal else "non_causal"] = {"us": round(dt * 1e6, 1)}
+    out["sample"] = "the whole tiny workload (B=1 H=2 N=128 d=64 fp16), mean of 20 calls"
+    return out
+
+
+def cpu_baseline_subset(name, cores, n_rows, seed):
+    """The oracle on a seeded subset of rows of a large prefill workload; the
+    full workload's time is extrapolated by the subset's share of its flops."""
+    import numpy as np
+
+    import oracle
+    from exact_attention_46_amd import workloads as wl
+
+    w = wl.WORKLOADS[name]
+    q, k, v = (wl.bits(t) for t in wl.workload_prefill_inputs(w))
+    rng = np.random.default_rng(seed)
+    rows = np.stack([rng.integers(0, w.B, n_rows), rng.integers(0, w.Hq, n_rows),
+                     rng.integers(0, w.N, n_rows)], axis=1).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.attn_fwd_rows(q, k, v, 0, w.scale, True, rows, nthreads=cores)
+    dt = time.perf_counter() - t0
+    fl = _rows_flops(rows, w.N, w.d)
+    full = 4.0 * w.B * w.Hq * w.N * w.N * w.d / 2.0
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "sample": "%d seeded random query rows (%.3f %% of the workload's flops), %.2f s"
+                      % (n_rows, 100.0 * fl / full, dt),
+            "seconds": dt,
+            "est_full_seconds": round(dt * full / fl, 1),
+            "extrapolation": "full time = subset time x (workload flops / subset flops)"}
 
 
 def _cpu_model():
@@ -495,6 +552,94 @@ def bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream):
                          "traffic": load_traffic("attn_decode_split_kernel/decode_paged")}}
 
 
+def bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream, paged):
+    """The decode workload at its 512-key chunks with the combine fused into the
+    split kernel (one launch, no separate combine), contiguous or paged (64-row
+    pages of a shuffled pool). Timed in a loop of its own."""
+    print("bench: fused decode%s" % (" (paged)" if paged else ""), file=sys.stderr, flush=True)
+    B, Hq, d = dq.shape
+    o = torch.empty((B, Hq, d), dtype=dq.dtype, device=dq.device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dq.device)
+    if paged:
+        kp, vp, table = wl.paged_from_padded(kc, vc, sl, PAGE_SIZE, seed=wd.seed)
+        td = table.to(kc.device)
+        ws = ea.fused_workspace(B, Hq, kc.shape[1], table.shape[1] * PAGE_SIZE, d, wd.chunk,
+                                dq.device)
+
+        def run():
+            ea.attn_decode_fused_paged(dq, kp, vp, td, sld, o, lse, ws, wd.chunk, wd.scale,
+                                       stream)
+    else:
+        ws = ea.fused_workspace(B, Hq, kc.shape[1], kc.shape[2], d, wd.chunk, dq.device)
+
+        def run():
+            ea.attn_decode_fused(dq, kc, vc, sld, o, lse, ws, wd.chunk, wd.scale, stream)
+
+    for _ in range(max(1, args.warmup)):
+        run()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in events:
+        e[0].record(stream)
+        run()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    lens = sl.numpy().astype(np.int64)
+    kv_bytes = float(np.sum(2 * wd.Hkv * lens * wd.d * 2))
+    gbs = kv_bytes / (ms * 1e-3) / 1e9
+    kern = "attn_decode_split_kernel<bf16,128,%sfused>" % ("paged," if paged else "")
+    return {"value": round(gbs, 1), "unit": "GB/s", "ms": round(ms, 4), "chunk": wd.chunk,
+            "roofline": {"kernel": kern, "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("attn_decode_split_kernel/decode_fused"
+                                                 + ("_paged" if paged else ""))}}
+
+
+def bench_tiny(args, torch, np, ea, wl, dev, stream):
+    """The tiny fp16 workload, causal and not: microseconds per forward (events
+    around a loop of back-to-back calls; launch-bound, no roofline claim)."""
+    print("bench: tiny workload", file=sys.stderr, flush=True)
+    w = wl.WORKLOADS["tiny"]
+    q, k, v = (t.to(dev) for t in wl.workload_prefill_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    out = {"unit": "us", "shape": {"B": w.B, "H": w.Hq, "N": w.N, "d": w.d, "dtype": "fp16"}}
+    for causal in (False, True):
+        for _ in range(50):
+            ea.attn_fwd(q, k, v, o, lse, causal, w.scale, stream)
+        torch.cuda.synchronize()
+        reps = 200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            ea.attn_fwd(q, k, v, o, lse, causal, w.scale, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out["causal_us" if causal else "non_causal_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    return out
+
+
+def run_only(args, torch, np, ea, wl, wp, wd, dev):
+    """One measurement alone (bench.py --only NAME), for counter runs: the
+    kernels of that measurement only, so that each profiled dispatch belongs
+    to one workload."""
+    stream = torch.cuda.current_stream()
+    name = args.only
+    if name in ("fwd_gqa_prefill", "fwd_long_context"):
+        return {name: bench_fwd_workload(args, torch, np, ea, wl, name[4:], dev, stream)}
+    if name in ("bwd", "fwd_local"):
+        q, k, v = (t.to(dev) for t in wl.workload_prefill_inputs(wp))
+        if name == "fwd_local":
+            return {name: bench_local(args, torch, np, ea, wp, q, k, v, stream)}
+        o, lse = ea.fwd(q, k, v, causal=True, scale=wp.scale)
+        return {name: bench_bwd(args, torch, np, ea, wp, q, k, v, o, lse, stream)}
+    sl, dq, kc, vc = wl.workload_decode_inputs(wd, device=dev)
+    dq, sld = dq.to(dev), sl.to(dev)
+    return {name: bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream,
+                                     paged=(name == "decode_fused_paged"))}
+
+
 def main():
     args = parse()
     if args.record_traffic:
@@ -518,6 +663,9 @@ def main():
 
     wp = wl.WORKLOADS["llm_prefill"]
     wd = wl.WORKLOADS["decode"]
+    if args.only in ONLY_EXTRA:
+        print(json.dumps(run_only(args, torch, np, ea, wl, wp, wd, dev)), flush=True)
+        return
     do_pre = args.only in ("all", "prefill")
     do_dec = args.only in ("all", "decode")
 
@@ -642,12 +790,25 @@ def main():
     if do_dec and not args.no_paged:
         out["decode_paged"] = bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc,
                                           stream)
+    if do_dec and not args.no_fused:
+        out["decode_fused"] = bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc,
+                                                 stream, paged=False)
+        if not args.no_paged:
+            out["decode_fused_paged"] = bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq,
+                                                           sld, kc, vc, stream, paged=True)
+    if do_pre and not args.no_configs:
+        out["fwd_tiny"] = bench_tiny(args, torch, np, ea, wl, dev, stream)
     if not args.no_cpu_baseline and do_pre:
         print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wp, q, k, v, args.cpu_seconds)
+        cb = cpu_baseline(wp, q, k, v, args.cpu_seconds)
+        cores = cb["cores"]
+        cb["tiny"] = cpu_baseline_tiny(cores)
+        if not args.no_configs:
+            cb["gqa_prefill"] = cpu_baseline_subset("gqa_prefill", cores, 2048, 21)
+            cb["long_context"] = cpu_baseline_subset("long_context", cores, 512, 22)
         if do_dec:
-            out["cpu_baseline"]["decode"] = cpu_baseline_decode(wd, sl, dq, kc, vc,
-                                                                out["cpu_baseline"]["cores"])
+            cb["decode"] = cpu_baseline_decode(wd, sl, dq, kc, vc, cores)
+        out["cpu_baseline"] = cb
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

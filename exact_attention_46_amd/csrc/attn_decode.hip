@@ -402,64 +402,78 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   };
 
   // Fused form: the merge of pair (b, g) by the wave that completed its count.
-  // Lanes take (head r, 4 consecutive d values) pieces, 64 at a time; each
-  // reads the pair's nc chunk LSEs and partial outputs with device-scope loads
-  // (issued in batches, then used): M = max LSE_c, w_c = exp(LSE_c - M),
-  // O = sum w_c O_c / sum w_c (rounded to the dtype), LSE = M + log sum w_c
-  // (the two passes of the aprender-gpu reduce kernel; chunks with LSE = -inf
-  // carry no weight). Then the counter is set back to zero for the next call.
+  // Lanes take (head r, 4 consecutive d values) pieces, up to two each per
+  // round (128 pieces: all of them at R * d <= 512), and read the pair's nc
+  // chunk LSEs and partial outputs with device-scope loads, 16 chunks per
+  // batch of loads in flight, in one pass with a running maximum (the rescaling
+  // combine of the aprender-gpu reduce kernel done online): M = max LSE_c,
+  // w_c = exp(LSE_c - M), O = sum w_c O_c / sum w_c (rounded to the dtype),
+  // LSE = M + log sum w_c; chunks with LSE = -inf carry no weight. Then the
+  // counter is set back to zero for the next call.
   auto merge = [&](int b, int g, int nc) {
     constexpr int CPH = D / 4;  // 16-byte pieces per head
     constexpr int MB = 16;      // chunks per batch of loads
     const auto ro = pair_rsrc_o(b, g);
     const auto rl = pair_rsrc_l(b, g);
     const int64_t row0 = (int64_t)b * Hq + (int64_t)g * R;
-    for (int p0 = 0; p0 < R * CPH; p0 += 64) {
-      const int pp = p0 + lane;
-      const bool on = pp < R * CPH;
-      const int r = on ? pp / CPH : 0;
-      const int c4 = pp % CPH;
-      const uint32_t vl = (uint32_t)r * (uint32_t)C * 4u;
-      const uint32_t vo = (uint32_t)r * (uint32_t)C * (uint32_t)(D * 4) + (uint32_t)c4 * 16u;
-      float M = -INFINITY;
-      for (int c0 = 0; c0 < nc; c0 += MB) {
-        float lc[MB];
+    for (int p0 = 0; p0 < R * CPH; p0 += 128) {
+      uint32_t vl[2], vo[2];
+      int rr[2], c4[2];
+      bool on[2];
 #pragma unroll
-        for (int u = 0; u < MB; ++u)
-          lc[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rl, vl, min(c0 + u, nc - 1) * 4, kDeviceScope));
-#pragma unroll
-        for (int u = 0; u < MB; ++u) M = fmaxf(M, lc[u]);
+      for (int u = 0; u < 2; ++u) {
+        const int pp = p0 + 64 * u + lane;
+        on[u] = pp < R * CPH;
+        rr[u] = on[u] ? pp / CPH : 0;
+        c4[u] = pp % CPH;
+        vl[u] = (uint32_t)rr[u] * (uint32_t)C * 4u;
+        vo[u] = (uint32_t)rr[u] * (uint32_t)C * (uint32_t)(D * 4) + (uint32_t)c4[u] * 16u;
       }
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      float wsum = 0.f;
-      if (M != -INFINITY) {
-        for (int c0 = 0; c0 < nc; c0 += MB) {
-          float lc[MB];
-          f32x4_t x[MB];
+      float M[2] = {-INFINITY, -INFINITY}, wsum[2] = {0.f, 0.f};
+      f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+      for (int c0 = 0; c0 < nc; c0 += MB) {
+        float lc[2][MB];
+        f32x4_t x[2][MB];
 #pragma unroll
-          for (int u = 0; u < MB; ++u) {
-            const int c = min(c0 + u, nc - 1);
-            lc[u] = __uint_as_float(
-                __builtin_amdgcn_raw_buffer_load_b32(rl, vl, c * 4, kDeviceScope));
-            x[u] = __builtin_bit_cast(
-                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, vo, c * (D * 4), kDeviceScope));
+        for (int j = 0; j < MB; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int c = min(c0 + j, nc - 1);
+            lc[u][j] = __uint_as_float(
+                __builtin_amdgcn_raw_buffer_load_b32(rl, vl[u], c * 4, kDeviceScope));
+            x[u][j] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ro, vo[u], c * (D * 4), kDeviceScope));
           }
 #pragma unroll
-          for (int u = 0; u < MB; ++u) {
-            // chunks past nc (the batch's clamped repeats) and empty chunks: no weight
-            const float w = (c0 + u >= nc || lc[u] == -INFINITY)
-                                ? 0.f : fast_exp2((lc[u] - M) * kLog2e);
-            acc += w * x[u];
-            wsum += w;
+        for (int u = 0; u < 2; ++u) {
+          float mb = M[u];
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            if (c0 + j < nc) mb = fmaxf(mb, lc[u][j]);
+          if (mb == -INFINITY) continue;
+          const float alpha = M[u] == -INFINITY ? 0.f : fast_exp2((M[u] - mb) * kLog2e);
+          acc[u] *= alpha;
+          wsum[u] *= alpha;
+          M[u] = mb;
+#pragma unroll
+          for (int j = 0; j < MB; ++j) {
+            // the batch's clamped repeats past nc, and empty chunks: no weight
+            const float w = (c0 + j >= nc || lc[u][j] == -INFINITY)
+                                ? 0.f : fast_exp2((lc[u][j] - mb) * kLog2e);
+            acc[u] += w * x[u][j];
+            wsum[u] += w;
           }
         }
       }
-      if (on) {
-        const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-        *reinterpret_cast<u32x2_t*>(o_fin + (row0 + r) * D + 4 * c4) =
-            (u32x2_t){pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
-        if (c4 == 0) lse_fin[row0 + r] = wsum > 0.f ? M + kLn2 * fast_log2(wsum) : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if (!on[u]) continue;
+        const float inv = wsum[u] > 0.f ? 1.f / wsum[u] : 0.f;
+        *reinterpret_cast<u32x2_t*>(o_fin + (row0 + rr[u]) * D + 4 * c4[u]) =
+            (u32x2_t){pack2<DT>(acc[u][0] * inv, acc[u][1] * inv),
+                      pack2<DT>(acc[u][2] * inv, acc[u][3] * inv)};
+        if (c4[u] == 0)
+          lse_fin[row0 + rr[u]] = wsum[u] > 0.f ? M[u] + kLn2 * fast_log2(wsum[u]) : -INFINITY;
       }
     }
     if (lane == 0)
