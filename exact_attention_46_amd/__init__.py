@@ -12,6 +12,7 @@ from ._binding import (  # noqa: F401
     EXPORTS,
     LIB_PATH,
     attn_bwd,
+    attn_bwd_noalloc,
     attn_decode,
     attn_decode_combine,
     attn_decode_fused,

@@ -26,8 +26,10 @@ ERR_UNSUPPORTED = -3
 ERR_MISALIGNED = -4
 ERR_BAD_ARG = -5
 ERR_HIP = -6
+ERR_SCRATCH = -7
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_fwd_qkvpacked", "attn_bwd",
+           "attn_bwd_noalloc",
            "attn_decode_split",
            "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
            "attn_decode_workspace", "attn_decode_fused", "attn_decode_fused_paged",
@@ -58,6 +60,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_local.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, i, p]
         lib.attn_fwd_qkvpacked.argtypes = [p, p, p, i, i, i, i, f, i, i, p]
         lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
+        lib.attn_bwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         ll = ctypes.c_longlong
         lib.attn_decode.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, f, i, p]
         lib.attn_decode_workspace.argtypes = [i, i, i, i, i]
@@ -75,6 +78,7 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_local.restype = i
         lib.attn_fwd_qkvpacked.restype = i
         lib.attn_bwd.restype = i
+        lib.attn_bwd_noalloc.restype = i
         lib.attn_decode.restype = i
         lib.attn_decode_workspace.restype = ctypes.c_longlong
         lib.attn_decode_split.restype = i
@@ -214,6 +218,29 @@ def attn_bwd(q, k, v, o, dout, lse, delta, dq, dk, dv, causal: bool, scale: floa
                                  float(scale), int(bool(causal)), _dtype_code(q), _stream(stream))
     if st != OK:
         raise AttnError("attn_bwd", st)
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float,
+                     stream=None) -> None:
+    """Calls attn_bwd_noalloc: attn_bwd with D in the library's fixed scratch (no
+    delta argument, nothing allocated; B*Hq*Nq at most 4194304)."""
+    _gpu(q, k, v, o, dout, lse, dq, dk, dv)
+    _need(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D, k ~ v")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape[0] == B and k.shape[3] == d, "k/v batch or head dim differ from q")
+    for t in (k, v, o, dout, dq, dk, dv):
+        _need(t.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape and dout.shape == q.shape and dq.shape == q.shape,
+          "o, dout, dq must have q's shape")
+    _need(dk.shape == k.shape and dv.shape == k.shape, "dk, dv must have k's shape")
+    _need(lse.dtype == torch.float32 and tuple(lse.shape) == (B, Hq, Nq), "lse [B,Hq,Nq] fp32")
+    st = load_library().attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                         _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq,
+                                         Nk, d, float(scale), int(bool(causal)), _dtype_code(q),
+                                         _stream(stream))
+    if st != OK:
+        raise AttnError("attn_bwd_noalloc", st)
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, stream=None):

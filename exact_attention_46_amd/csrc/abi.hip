@@ -82,24 +82,52 @@ extern "C" int attn_fwd_local(const void* q, const void* k, const void* v, void*
   return from_hip(mi355attn::launch_fwd(a, static_cast<hipStream_t>(stream)));
 }
 
-extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, float* delta, void* dq, void* dk,
-                        void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
-                        int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !delta || !dq || !dk || !dv)
-    return MI355ATTN_ERR_NULL_PTR;
+namespace {
+
+// Checks shared by attn_bwd and attn_bwd_noalloc (delta excepted).
+int bwd_status(const void* q, const void* k, const void* v, const void* o, const void* dout,
+               const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq,
+               int Nk, int d, float scale, int causal, int dtype) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return MI355ATTN_ERR_NULL_PTR;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return MI355ATTN_ERR_BAD_SHAPE;
   if (Hq % Hkv != 0 || Nq > kMaxSeq || Nk > kMaxSeq) return MI355ATTN_ERR_BAD_SHAPE;
   if (!head_dim_ok(d) || !dtype_ok(dtype)) return MI355ATTN_ERR_UNSUPPORTED;
   if (!scale_ok(scale) || (causal != 0 && causal != 1)) return MI355ATTN_ERR_BAD_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
-      !aligned(lse, 4) || !aligned(delta, 4))
+      !aligned(lse, 4))
     return MI355ATTN_ERR_MISALIGNED;
   if (mi355attn::bwd_grid_blocks(B, Hq, Hkv, Nq, Nk) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  return MI355ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, float* delta, void* dq, void* dk,
+                        void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                        int causal, int dtype, void* stream) {
+  if (!delta) return MI355ATTN_ERR_NULL_PTR;
+  const int st = bwd_status(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                            causal, dtype);
+  if (st != MI355ATTN_OK) return st;
+  if (!aligned(delta, 4)) return MI355ATTN_ERR_MISALIGNED;
   mi355attn::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
                        causal, dtype};
   return from_hip(mi355attn::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                                int causal, int dtype, void* stream) {
+  const int st = bwd_status(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                            causal, dtype);
+  if (st != MI355ATTN_OK) return st;
+  if ((int64_t)B * Hq * Nq > mi355attn::kBwdScratchFloats) return MI355ATTN_ERR_SCRATCH;
+  mi355attn::BwdArgs a{q, k, v, o, dout, lse, nullptr, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                       causal, dtype};
+  return from_hip(mi355attn::launch_bwd_noalloc(a, static_cast<hipStream_t>(stream)));
 }
 
 extern "C" int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -359,6 +387,9 @@ extern "C" const char* attn_status_str(int status) {
     case MI355ATTN_ERR_MISALIGNED: return "misaligned pointer (16 bytes for tensors, 4 for lse/lens)";
     case MI355ATTN_ERR_BAD_ARG: return "bad argument: scale must be finite and > 0, causal 0 or 1";
     case MI355ATTN_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case MI355ATTN_ERR_SCRATCH:
+      return "the problem needs more than the library's fixed scratch (attn_bwd_noalloc: "
+             "B * Hq * Nq above 4194304)";
     default: return "unknown status";
   }
 }

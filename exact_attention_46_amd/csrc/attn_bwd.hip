@@ -42,6 +42,8 @@
 // instead of 5), which is what removes the atomics on dQ.
 #include <type_traits>
 
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -594,6 +596,46 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
                      (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+
+// attn_bwd_noalloc keeps D (one float per query row) here instead of in a
+// caller-provided buffer: callers that cannot allocate (graph capture, tight
+// serving loops) get a backward that allocates nothing. Every GPU the library
+// runs on holds its own copy (16 MiB) until the process ends; all calls on
+// one GPU share it, and the dQ kernel writes every D it holds before the
+// dK/dV kernel reads it, so no clearing is needed.
+static __device__ __align__(256) float scratch[kBwdScratchFloats];
+
+// This GPU's address of `scratch`, looked up once per device (with that
+// device current) on the first call there. The host-side name `scratch` is a
+// stand-in for the symbol, never a device address; only the looked-up pointer
+// is passed to kernels.
+static hipError_t bwd_scratch(float** out) {
+  static std::atomic<float*> cached[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  float* p = cached[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    cached[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_noalloc(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
+  hipError_t e = bwd_scratch(&a.delta);
+  if (e != hipSuccess) return e;
+  return launch_bwd(a, stream);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {

@@ -93,8 +93,14 @@ int decode_chunk_policy(int B, int Hkv, int max_len);
 // Largest grid of the three backward launches.
 int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk);
 
+// Floats of the library's fixed backward scratch on each GPU (attn_bwd_noalloc:
+// one per query row, so B * Hq * Nq must not exceed it).
+constexpr int64_t kBwdScratchFloats = int64_t(1) << 22;
+
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
+// launch_bwd with a.delta replaced by the fixed scratch of the current device.
+hipError_t launch_bwd_noalloc(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

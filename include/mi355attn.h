@@ -47,6 +47,7 @@ extern "C" {
 #define MI355ATTN_ERR_MISALIGNED (-4)  /* a pointer breaks the alignment rule above */
 #define MI355ATTN_ERR_BAD_ARG (-5)     /* scale not finite or <= 0, causal not 0/1 */
 #define MI355ATTN_ERR_HIP (-6)         /* the HIP runtime reported an error at launch */
+#define MI355ATTN_ERR_SCRATCH (-7)     /* larger than the fixed scratch of attn_bwd_noalloc */
 
 /*
  * attn_fwd — exact attention forward with per-row log-sum-exp.
@@ -134,6 +135,27 @@ int attn_fwd_local(const void* q, const void* k, const void* v, void* o, float* 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int Hq, int Hkv,
              int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
+
+/*
+ * attn_bwd_noalloc — attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * it): the same kernels and the same result, with D kept in a fixed scratch
+ * array inside the library instead of the caller's delta buffer. Nothing is
+ * allocated by the call.
+ *
+ *   arguments as attn_bwd, without delta.
+ *
+ * The scratch holds 4194304 floats (16 MiB) on each GPU the library runs on,
+ * from the first call there until the process ends; B * Hq * Nq above that
+ * returns MI355ATTN_ERR_SCRATCH before any HIP call. Every call on one GPU
+ * uses the same scratch (each call rewrites what it reads), so calls that
+ * overlap in time on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.
+ */
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                     void* stream);
 
 /*
  * attn_fwd_varlen — attn_fwd over a packed batch of sequences of different

@@ -58,6 +58,7 @@ def test_status_codes_match_header(lib):
     assert d["MI355ATTN_ERR_MISALIGNED"] == ea._binding.ERR_MISALIGNED
     assert d["MI355ATTN_ERR_BAD_ARG"] == ea._binding.ERR_BAD_ARG
     assert d["MI355ATTN_ERR_HIP"] == ea._binding.ERR_HIP
+    assert d["MI355ATTN_ERR_SCRATCH"] == ea._binding.ERR_SCRATCH
     assert d["MI355ATTN_BF16"] == 0 and d["MI355ATTN_FP16"] == 1
     for code in range(-6, 1):
         s = ea.attn_status_str(code)
@@ -103,6 +104,24 @@ def bwd(lib, q=A, k=A, v=A, o=A, do=A, lse=A2, delta=A2, dq=A, dk=A, dv=A, B=1, 
 ])
 def test_attn_bwd_rejects(lib, kw, code):
     assert bwd(lib, **kw) == code
+
+
+def bwd_noalloc(lib, q=A, k=A, v=A, o=A, do=A, lse=A2, dq=A, dk=A, dv=A, B=1, Hq=2, Hkv=2,
+                Nq=8, Nk=8, d=128, scale=0.1, causal=1, dtype=0):
+    return lib.attn_bwd_noalloc(q, k, v, o, do, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                                causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(dv=None), -1),
+    (dict(B=0), -2), (dict(Hq=3, Hkv=2), -2), (dict(Nq=2**23 + 1), -2),
+    (dict(d=32), -3), (dict(dtype=5), -3),
+    (dict(scale=0.0), -5), (dict(causal=2), -5), (dict(do=MIS), -4),
+    # one D per query row: at most 2^22 rows fit the fixed scratch
+    (dict(B=1, Hq=33, Hkv=1, Nq=2**17), -7), (dict(B=2, Hq=32, Hkv=8, Nq=2**16 + 1), -7),
+])
+def test_attn_bwd_noalloc_rejects(lib, kw, code):
+    assert bwd_noalloc(lib, **kw) == code
 
 
 def fwd_varlen(lib, q=A, k=A, v=A, o=A2, lse=A2, cq=A, ck=A2, B=3, Hq=4, Hkv=2, total_q=100,
