@@ -48,8 +48,15 @@ METRIC = "attn fwd TFLOP/s (bf16, d=128, causal) + split-KV decode KV GB/s"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CUs x 4096 dense bf16 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "exact_attention_46_amd", "csrc", f)
-                  for f in ("common.hpp", "attn_fwd.hip", "attn_decode.hip")]
+# The sources each recorded kernel is built from (a recorded traffic figure is
+# used only while they are unchanged).
+_CSRC = os.path.join(ROOT, "exact_attention_46_amd", "csrc")
+KERNEL_SOURCES = {
+    "attn_fwd_kernel": ["common.hpp", "attn_fwd.hip"],
+    "attn_decode_split_kernel": ["common.hpp", "attn_decode.hip"],
+    "attn_bwd_dq_kernel": ["common.hpp", "attn_bwd.hip"],
+    "attn_bwd_dkdv_kernel": ["common.hpp", "attn_bwd.hip"],
+}
 
 
 def parse():
@@ -84,9 +91,10 @@ def parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run a plain streaming kernel of known size "
                          "(the calibration of HBM byte counters)")
-    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "RUN"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "'bench.py --copy-calibration' into " + TRAFFIC_FILE)
+                         "'bench.py --copy-calibration' (RUN = step) or 'bench.py --only RUN "
+                         "--copy-calibration' into entries of " + TRAFFIC_FILE)
     return ap.parse_args()
 
 
@@ -127,10 +135,31 @@ def _counter_means(folder, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
-def record_traffic(fetch_dir, write_dir):
-    """HBM bytes per launch of the timed kernels: FETCH_SIZE and WRITE_SIZE (KiB per
+# Kernels whose HBM traffic a profiled run records: run -> [(entry, kernel-name match)].
+# Every run holds the calibration kernel too.
+TRAFFIC_RUNS = {
+    "step": [("attn_fwd_kernel/llm_prefill", "attn_fwd_kernel"),
+             ("attn_decode_split_kernel/decode", "attn_decode_split_kernel<0, 128, false, false, false>"),
+             ("attn_decode_split_kernel/decode_paged",
+              "attn_decode_split_kernel<0, 128, true, false, false>")],
+    "fwd_gqa_prefill": [("attn_fwd_kernel/gqa_prefill", "attn_fwd_kernel")],
+    "fwd_long_context": [("attn_fwd_kernel/long_context", "attn_fwd_kernel")],
+    "fwd_local": [("attn_fwd_kernel/local", "attn_fwd_kernel<0, 128, false, false, true>")],
+    "bwd": [("attn_bwd_dq_kernel/llm_prefill", "attn_bwd_dq_kernel"),
+            ("attn_bwd_dkdv_kernel/llm_prefill", "attn_bwd_dkdv_kernel")],
+    "decode_fused": [("attn_decode_split_kernel/decode_fused",
+                      "attn_decode_split_kernel<0, 128, false, false, true>")],
+    "decode_fused_paged": [("attn_decode_split_kernel/decode_fused_paged",
+                            "attn_decode_split_kernel<0, 128, true, false, true>")],
+}
+
+
+def record_traffic(fetch_dir, write_dir, run):
+    """HBM bytes per launch of a run's kernels: FETCH_SIZE and WRITE_SIZE (KiB per
     dispatch), each divided by what the same counter reads per byte of the
-    calibration kernel."""
+    calibration kernel; merged into the traffic file."""
+    if run not in TRAFFIC_RUNS:
+        raise SystemExit("unknown run %r (one of %s)" % (run, ", ".join(TRAFFIC_RUNS)))
     fetch = _counter_means(fetch_dir, "FETCH_SIZE")
     write = _counter_means(write_dir, "WRITE_SIZE")
 
@@ -142,28 +171,31 @@ def record_traffic(fetch_dir, write_dir):
 
     f_cal = pick(fetch, COPY_CAL_MATCH) * 1024.0 / COPY_CAL_BYTES
     w_cal = pick(write, COPY_CAL_MATCH) * 1024.0 / COPY_CAL_BYTES
-    rec = {"_calibration": {"kernel": "torch.neg over %d bytes of bf16" % COPY_CAL_BYTES,
-                            "fetch_counter_bytes_per_byte": round(f_cal, 4),
-                            "write_counter_bytes_per_byte": round(w_cal, 4)}}
-    for name, match in (("attn_fwd_kernel/llm_prefill", "attn_fwd_kernel"),
-                        ("attn_decode_split_kernel/decode",
-                         "attn_decode_split_kernel<0, 128, false, false>"),
-                        ("attn_decode_split_kernel/decode_paged",
-                         "attn_decode_split_kernel<0, 128, true, false>")):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        rec = {}
+    rec.setdefault("_calibration", {})[run] = {
+        "kernel": "torch.neg over %d bytes of bf16" % COPY_CAL_BYTES,
+        "fetch_counter_bytes_per_byte": round(f_cal, 4),
+        "write_counter_bytes_per_byte": round(w_cal, 4)}
+    for name, match in TRAFFIC_RUNS[run]:
         fb = pick(fetch, match) * 1024.0 / f_cal
         wb = pick(write, match) * 1024.0 / w_cal
         rec[name] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
-                     "bytes_per_launch": round(fb + wb), "source_hash": source_hash()}
+                     "bytes_per_launch": round(fb + wb), "source_hash": source_hash(name)}
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
-    print(json.dumps(rec, indent=1))
+    print(json.dumps({k: rec[k] for k, _ in TRAFFIC_RUNS[run]}, indent=1))
 
 
-def source_hash():
+def source_hash(entry):
+    """Hash of the sources of the kernel a traffic entry ("kernel/workload") names."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
+    for name in KERNEL_SOURCES[entry.split("/")[0]]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -177,7 +209,7 @@ def load_traffic(kernel: str):
     except (OSError, ValueError):
         return None
     ent = rec.get(kernel)
-    if not ent or ent.get("source_hash") != source_hash():
+    if not ent or ent.get("source_hash") != source_hash(kernel):
         return None
     return ent.get("bytes_per_launch")
 
@@ -378,7 +410,13 @@ def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
             "flop_convention": "2.5 x forward (causal halved)",
             "roofline": {"kernel": "attn_bwd (dq + dkdv kernels)", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": _bwd_traffic()}}
+
+
+def _bwd_traffic():
+    a = load_traffic("attn_bwd_dq_kernel/llm_prefill")
+    b = load_traffic("attn_bwd_dkdv_kernel/llm_prefill")
+    return a + b if a is not None and b is not None else None
 
 
 LOCAL_WINDOW = 512
@@ -412,7 +450,8 @@ def bench_local(args, torch, np, ea, wp, qg, kg, vg, stream):
             "window": [LOCAL_WINDOW, 0],
             "roofline": {"kernel": "attn_fwd_kernel<bf16,128,local>", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("attn_fwd_kernel/local")}}
 
 
 def bench_fwd_workload(args, torch, np, ea, wl, name, dev, stream):
@@ -444,7 +483,10 @@ def bench_fwd_workload(args, torch, np, ea, wl, name, dev, stream):
             "shape": {"B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "N": w.N, "d": w.d, "causal": True},
             "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal>", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("attn_fwd_kernel/" + name),
+                         "algorithmic_bytes": (2 * w.B * w.Hq * w.N + 2 * w.B * w.Hkv * w.N) * w.d
+                         * 2 + w.B * w.Hq * w.N * 4}}
 
 
 def bench_qkvpacked(args, torch, np, ea, wp, stream):
@@ -664,7 +706,10 @@ def main():
     wp = wl.WORKLOADS["llm_prefill"]
     wd = wl.WORKLOADS["decode"]
     if args.only in ONLY_EXTRA:
-        print(json.dumps(run_only(args, torch, np, ea, wl, wp, wd, dev)), flush=True)
+        res = run_only(args, torch, np, ea, wl, wp, wd, dev)
+        if args.copy_calibration:
+            copy_calibration(torch, dev)
+        print(json.dumps(res), flush=True)
         return
     do_pre = args.only in ("all", "prefill")
     do_dec = args.only in ("all", "decode")

@@ -74,7 +74,11 @@ struct FwdLayout {
   static constexpr int kQWave = 32 * kRow;           // one wave's Q rows
   static constexpr int kQLoads = 32 / kRowsPerLoad;  // loads per wave for them
   static constexpr int kLds = 4 * kTile + kFwdWaves * kQWave;  // K, V (two each), Q
+  // Local attention: two K/V rings (one per 128-row half), Q straight to registers.
+  static constexpr int kLdsLocal = 8 * kTile;
 };
+static_assert(FwdLayout<128>::kLds <= 160 * 1024 && FwdLayout<128>::kLdsLocal <= 160 * 1024,
+              "LDS of a gfx950 workgroup");
 
 // Chunk swizzles (chunk index XOR f(row)), chosen against the LDS bank layout
 // (64 four-byte banks; a 256-byte window is one bank row):
@@ -170,7 +174,8 @@ __device__ __forceinline__ float widen16(uint32_t w, int hi) {
 // LOCAL = true: the mask is the window `win` (CAUSAL is false then); each
 // workgroup walks only the key tiles its rows' windows touch, and each wave
 // only the range of them its own rows touch.
-template <int DT, int D, bool CAUSAL, bool VARLEN, bool LOCAL>
+// SPLIT (with LOCAL only): the two-halves form below, for narrow windows.
+template <int DT, int D, bool CAUSAL, bool VARLEN, bool LOCAL, bool SPLIT = false>
 __global__ void __launch_bounds__(kFwdThreads, 1)
 attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                 const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
@@ -180,7 +185,8 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   constexpr int DS = D / 16;   // MFMA k-steps over d
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   constexpr int ROW = Lay::kRow;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[Lay::kLds];
+  static_assert(LOCAL || !SPLIT, "the two-halves form is for local attention");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SPLIT ? Lay::kLdsLocal : Lay::kLds];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,26 +245,48 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   const auto rq = VARLEN ? make_rsrc(qh + (int64_t)q0 * QS, (uint32_t)(q_rows - 1) * QS * 2 + ROW)
                          : make_rsrc(qh, (uint32_t)Nq * ROW);
 
-  // Keys this workgroup can see: [kv_begin, kv_end); its tiles t0 .. n_tiles-1.
-  int kv_end = Nk;
-  if (CAUSAL) {
-    kv_end = min(q0 + kFwdBM, Nq) - 1 + off + 1;
-    kv_end = max(0, min(kv_end, Nk));
+  // Tile-sharing group: the whole workgroup, or (SPLIT) one of two halves of 4
+  // waves and 128 rows (waves 0, 4, 1, 5 and 2, 6, 3, 7: each half holds both
+  // roles on two SIMDs) with a K/V ring of its own. A sliding window's key range
+  // grows with the rows that share it; halving them cuts the keys walked per
+  // row for a 512-key window from 768 to 640, at the price of two rings of
+  // loads per iteration (worth it for narrow windows only).
+  constexpr int G_WAVES = SPLIT ? 4 : kFwdWaves;
+  constexpr int G_ROWS = 32 * G_WAVES;
+  const int grp = SPLIT ? ((wave & 3) >> 1) : 0;
+  const int wig = SPLIT ? 2 * (wave & 1) + role_b : wave;  // wave index inside the group
+  // Keys a group with first row gq0 can see: its tiles [gt0, gn).
+  auto group_tiles = [&](int gq0, int& gt0, int& gn) {
+    int kv_end = Nk, kv_begin = 0;
+    if (CAUSAL) kv_end = max(0, min(Nk, min(gq0 + G_ROWS, Nq) - 1 + off + 1));
+    if constexpr (LOCAL) {
+      if (win.right >= 0) kv_end = max(0, min(Nk, min(gq0 + G_ROWS, Nq) - 1 + off + win.right + 1));
+      if (win.left >= 0) kv_begin = max(0, gq0 + off - win.left);
+      if (gq0 >= Nq) kv_end = 0;  // a half past the last row reads nothing
+      if (kv_begin > kv_end) kv_begin = kv_end;
+    }
+    gt0 = LOCAL ? kv_begin / kFwdBN : 0;
+    gn = max(gt0, (kv_end + kFwdBN - 1) / kFwdBN);
+  };
+  int t0, n_tiles;
+  group_tiles(q0 + G_ROWS * grp, t0, n_tiles);
+  // Iterations of the tile loop: the larger count of the groups (all waves
+  // pass the same barriers; a group past its last tile only waits).
+  int n_iter = n_tiles - t0;
+  if constexpr (SPLIT) {
+    int o0, on;
+    group_tiles(q0 + G_ROWS * (1 - grp), o0, on);
+    n_iter = max(n_iter, on - o0);
   }
-  int kv_begin = 0;
-  if constexpr (LOCAL) {
-    if (win.right >= 0) kv_end = max(0, min(Nk, min(q0 + kFwdBM, Nq) - 1 + off + win.right + 1));
-    if (win.left >= 0) kv_begin = max(0, q0 + off - win.left);
-    if (kv_begin > kv_end) kv_begin = kv_end;
-  }
-  const int t0 = LOCAL ? kv_begin / kFwdBN : 0;
-  const int n_tiles = (kv_end + kFwdBN - 1) / kFwdBN;
 
   // ---- Q: the wave's 32 rows go HBM -> its own LDS block once, swizzled like
   // K (rows past Nq land as zeros); the Q^T operand of each product is read
   // from there (lane: row r32, d-chunk half * DS + ds), which keeps the
   // registers for the accumulators.
-  unsigned char* qslot = smem + 4 * Lay::kTile + wave * Lay::kQWave;
+  // SPLIT: no Q block (Q goes straight to registers); the epilogue stages O in
+  // the group's ring instead, free after the last tile.
+  unsigned char* qslot = SPLIT ? smem + grp * 4 * Lay::kTile + wig * Lay::kQWave
+                               : smem + 4 * Lay::kTile + wave * Lay::kQWave;
   auto issue_q = [&]() {
 #pragma unroll
     for (int i = 0; i < Lay::kQLoads; ++i) {
@@ -274,12 +302,12 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   // +RPL-1; lane p fills physical chunk p % C of row p / C, i.e. it loads
   // logical chunk (p % C) ^ swz(row). Offsets are relative to the tile's first
   // row, whose address is carried by the per-tile buffer resource.
-  constexpr int LPW = Lay::kLoadsPerWave;
   constexpr int RPL = Lay::kRowsPerLoad;
+  constexpr int LPW = kFwdBN / RPL / G_WAVES;  // loads per wave and tensor
   uint32_t koff[LPW], voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int row = (wave * LPW + i) * RPL + lane / Lay::kChunks;
+    const int row = (wig * LPW + i) * RPL + lane / Lay::kChunks;
     const int pc = lane % Lay::kChunks;
     const uint32_t rb = (uint32_t)row * (uint32_t)KS * 2;  // == row * ROW when dense
     koff[i] = rb + (uint32_t)((pc ^ k_swz<D>(row)) * 16);
@@ -293,22 +321,23 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     else
       return (uint32_t)(Nk - r0) * ROW;
   };
-  // LDS: K buffers at [0, 2*kTile), V buffers at [2*kTile, 4*kTile).
-  unsigned char* kbuf = smem;
-  unsigned char* vbuf = smem + 2 * Lay::kTile;
+  // LDS: K buffers at [0, 2*kTile), V buffers at [2*kTile, 4*kTile) (of the
+  // group's ring: SPLIT has two).
+  unsigned char* kbuf = smem + (SPLIT ? grp * 4 * Lay::kTile : 0);
+  unsigned char* vbuf = kbuf + 2 * Lay::kTile;
   auto issue_k = [&](int t) {
     const int r0 = t * kFwdBN;  // < Nk for every tile that is issued
     const auto rk = make_rsrc(kh + (int64_t)r0 * KS, tile_bytes(r0));
     unsigned char* dst = kbuf + (t & 1) * Lay::kTile;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buf_load16_lds(rk, dst + (wave * LPW + i) * 1024, koff[i]);
+    for (int i = 0; i < LPW; ++i) buf_load16_lds(rk, dst + (wig * LPW + i) * 1024, koff[i]);
   };
   auto issue_v = [&](int t) {
     const int r0 = t * kFwdBN;
     const auto rv = make_rsrc(vh + (int64_t)r0 * KS, tile_bytes(r0));
     unsigned char* dst = vbuf + (t & 1) * Lay::kTile;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) buf_load16_lds(rv, dst + (wave * LPW + i) * 1024, voff[i]);
+    for (int i = 0; i < LPW; ++i) buf_load16_lds(rv, dst + (wig * LPW + i) * 1024, voff[i]);
   };
 
   // ---- per-lane LDS operand offsets (relative to the tile base)
@@ -531,13 +560,22 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     issue_v(t0);
   }
   if (n_tiles > t0 + 1) issue_k(t0 + 1);
-  issue_q();
+  if constexpr (SPLIT) {
+    // Q^T operands straight from memory (rows past Nq read as zeros).
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+      qf[ds] = buf_load16(rq, (uint32_t)(qw0 + r32) * ROW + (uint32_t)((half * DS + ds) * 16));
+  } else {
+    issue_q();
+  }
   wait_all_memory();
   __syncthreads();
   // Q^T operand in registers: lane holds row r32, d-chunk half * DS + ds.
+  if constexpr (!SPLIT) {
 #pragma unroll
-  for (int ds = 0; ds < DS; ++ds)
-    qf[ds] = *reinterpret_cast<const u32x4_t*>(qslot + r32 * ROW + (((half * DS + ds) ^ kx) << 4));
+    for (int ds = 0; ds < DS; ++ds)
+      qf[ds] = *reinterpret_cast<const u32x4_t*>(qslot + r32 * ROW + (((half * DS + ds) ^ kx) << 4));
+  }
   auto loads = [&](int t) {
     if (t + 2 < n_tiles) issue_k(t + 2);
     if (t + 1 < n_tiles) issue_v(t + 1);
@@ -568,7 +606,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
       softmax(t0, st, pf);
     }
     __syncthreads();
-    for (int t = t0; t < n_tiles; ++t) {
+    for (int t = t0; t < t0 + n_iter; ++t) {
       loads(t);
       matrix_phase(t);
       phase_barrier();
@@ -579,7 +617,7 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   } else {
     if (active(t0)) qk(t0, st, false, t0);
     __syncthreads();
-    for (int t = t0; t < n_tiles; ++t) {
+    for (int t = t0; t < t0 + n_iter; ++t) {
       loads(t);
       if (active(t)) softmax(t, st, pf);
       phase_barrier();
@@ -625,15 +663,21 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
         // this lane's half of q.k (d-chunks half*DS .. +DS-1), then its partner's
         const uint16_t* kr = kh + (int64_t)j * KS + half * (D / 2);
         float part = 0.f;
-#pragma unroll 2
-        for (int ds = 0; ds < DS; ++ds) {
-          const u32x4_t kk = *reinterpret_cast<const u32x4_t*>(kr + 8 * ds);
-          const u32x4_t qq =
-              *reinterpret_cast<const u32x4_t*>(qrow + (((half * DS + ds) ^ kx) << 4));
+        auto dot8 = [&](const u32x4_t& qq, const u32x4_t& kk) {
 #pragma unroll
           for (int w = 0; w < 4; ++w)
             part = __builtin_fmaf(widen16<DT>(qq[w], 0), widen16<DT>(kk[w], 0),
                                   __builtin_fmaf(widen16<DT>(qq[w], 1), widen16<DT>(kk[w], 1), part));
+        };
+        if constexpr (SPLIT) {  // Q is in registers (this form keeps no Q block)
+#pragma unroll
+          for (int ds = 0; ds < DS; ++ds)
+            dot8(qf[ds], *reinterpret_cast<const u32x4_t*>(kr + 8 * ds));
+        } else {
+#pragma unroll 2
+          for (int ds = 0; ds < DS; ++ds)
+            dot8(*reinterpret_cast<const u32x4_t*>(qrow + (((half * DS + ds) ^ kx) << 4)),
+                 *reinterpret_cast<const u32x4_t*>(kr + 8 * ds));
         }
         const float sdot = sum_with_partner32(part);
         bool allowed = my_row < Nq && j <= row_kmax;
@@ -698,6 +742,13 @@ attn_fwd_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
   }
 }
 
+// The two-halves form of local attention: both window bounds set and a window
+// of at most 1024 keys (measured on gfx950 at N = 2048, d = 128: +5 % at 512
+// keys back, -8 % at 2048, where both halves load nearly the same tiles).
+static bool local_split(int left, int right) {
+  return left >= 0 && right >= 0 && (int64_t)left + right <= 1024;
+}
+
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqt = (a.Nq + kFwdBM - 1) / kFwdBM;
@@ -705,7 +756,12 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_stride, a.kv_stride, a.o_stride,
                   a.uniform_len};
   const Window win{a.window_left, a.window_right};
-  if (a.local) {
+  if (a.local && local_split(a.window_left, a.window_right)) {
+    hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, true, true>), dim3((unsigned)blocks),
+                       dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                       (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+                       a.scale, vl, win);
+  } else if (a.local) {
     hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, true>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,

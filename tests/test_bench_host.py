@@ -31,8 +31,10 @@ def _write_counters(folder, counter, rows):
 
 
 FWD = "void mi355attn::attn_fwd_kernel<0, 128, true, false, false>(unsigned short const*)"
-DEC = "void mi355attn::attn_decode_split_kernel<0, 128, false, false>(unsigned short const*)"
-PAG = "void mi355attn::attn_decode_split_kernel<0, 128, true, false>(unsigned short const*)"
+DEC = "void mi355attn::attn_decode_split_kernel<0, 128, false, false, false>(unsigned short const*)"
+PAG = "void mi355attn::attn_decode_split_kernel<0, 128, true, false, false>(unsigned short const*)"
+DQ = "void mi355attn::attn_bwd_dq_kernel<0, 128, true>(unsigned short const*)"
+DKDV = "void mi355attn::attn_bwd_dkdv_kernel<0, 128, true>(unsigned short const*)"
 CAL = "void at::native::vectorized_elementwise_kernel<neg_kernel>(int)"
 
 
@@ -47,10 +49,10 @@ def test_record_traffic_scales_by_the_calibration_kernel(tmp_path, monkeypatch):
                      (DEC, 4096.0), (DEC, 4096.0), (PAG, 5000.0)])
     _write_counters(tmp_path / "w", "WRITE_SIZE",
                     [(CAL, kib), (FWD, 64.0), (DEC, 16.0), (PAG, 32.0)])
-    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+    bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "step")
     rec = json.loads(out.read_text())
-    assert rec["_calibration"]["fetch_counter_bytes_per_byte"] == 0.5
-    assert rec["_calibration"]["write_counter_bytes_per_byte"] == 1.0
+    assert rec["_calibration"]["step"]["fetch_counter_bytes_per_byte"] == 0.5
+    assert rec["_calibration"]["step"]["write_counter_bytes_per_byte"] == 1.0
     fwd = rec["attn_fwd_kernel/llm_prefill"]
     assert fwd["fetch_bytes"] == 2000 * 1024 * 2 and fwd["write_bytes"] == 64 * 1024
     assert fwd["bytes_per_launch"] == fwd["fetch_bytes"] + fwd["write_bytes"]
@@ -62,6 +64,14 @@ def test_record_traffic_scales_by_the_calibration_kernel(tmp_path, monkeypatch):
     out.write_text(json.dumps(rec))
     assert bench.load_traffic("attn_fwd_kernel/llm_prefill") is None
     assert bench.load_traffic("no such kernel") is None
+    # a second run (the backward) adds its entries and keeps the others
+    _write_counters(tmp_path / "f2", "FETCH_SIZE", [(CAL, kib), (DQ, 10.0), (DKDV, 20.0)])
+    _write_counters(tmp_path / "w2", "WRITE_SIZE", [(CAL, kib), (DQ, 1.0), (DKDV, 2.0)])
+    bench.record_traffic(str(tmp_path / "f2"), str(tmp_path / "w2"), "bwd")
+    rec = json.loads(out.read_text())
+    assert rec["attn_bwd_dq_kernel/llm_prefill"]["bytes_per_launch"] == 10 * 1024 + 1024
+    assert "attn_decode_split_kernel/decode" in rec and "bwd" in rec["_calibration"]
+    assert bench._bwd_traffic() == 10 * 1024 + 1024 + 20 * 1024 + 2 * 1024
 
 
 def test_record_traffic_needs_exactly_one_match(tmp_path, monkeypatch):
@@ -70,5 +80,7 @@ def test_record_traffic_needs_exactly_one_match(tmp_path, monkeypatch):
     _write_counters(tmp_path / "f", "FETCH_SIZE", [(CAL, kib), (FWD, 1.0), (PAG, 1.0)])
     _write_counters(tmp_path / "w", "WRITE_SIZE", [(CAL, kib), (FWD, 1.0), (PAG, 1.0)])
     with pytest.raises(SystemExit):
-        bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"))
+        bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "step")
+    with pytest.raises(SystemExit):
+        bench.record_traffic(str(tmp_path / "f"), str(tmp_path / "w"), "no such run")
     assert not (tmp_path / "traffic.json").exists()

@@ -795,6 +795,11 @@ LOCAL = [
     (1, 4, 4, 400, 400, 64, "bf16", -1, 0),
     (1, 4, 4, 400, 400, 128, "bf16", 300, -1),
     (1, 2, 2, 2048, 2048, 128, "bf16", 512, 0),
+    # windows above 1024 keys (or open on one side) take the one-group form,
+    # the others the two-halves form: both, at d = 64 and 128
+    (1, 4, 4, 2048, 2048, 128, "bf16", 1500, 0),
+    (1, 4, 2, 700, 700, 64, "fp16", 1000, 24),
+    (2, 4, 4, 1000, 1000, 64, "bf16", 1000, 25),
 ]
 
 
