@@ -144,7 +144,7 @@ TRAFFIC_RUNS = {
               "attn_decode_split_kernel<0, 128, true, false, false>")],
     "fwd_gqa_prefill": [("attn_fwd_kernel/gqa_prefill", "attn_fwd_kernel")],
     "fwd_long_context": [("attn_fwd_kernel/long_context", "attn_fwd_kernel")],
-    "fwd_local": [("attn_fwd_kernel/local", "attn_fwd_kernel<0, 128, false, false, true>")],
+    "fwd_local": [("attn_fwd_kernel/local", "attn_fwd_kernel<0, 128, false, false, true,")],
     "bwd": [("attn_bwd_dq_kernel/llm_prefill", "attn_bwd_dq_kernel"),
             ("attn_bwd_dkdv_kernel/llm_prefill", "attn_bwd_dkdv_kernel")],
     "decode_fused": [("attn_decode_split_kernel/decode_fused",
