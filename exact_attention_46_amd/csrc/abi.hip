@@ -1,7 +1,11 @@
 // C ABI of the attention library: argument checks, then one launch per call.
 // Every check runs before any HIP call, so a rejected call has no side effect.
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "../../include/mi355attn.h"
 #include "launch.hpp"
@@ -22,6 +26,28 @@ constexpr int kMaxSeq = 1 << 23;
 int from_hip(hipError_t e) { return e == hipSuccess ? MI355ATTN_OK : MI355ATTN_ERR_HIP; }
 
 }  // namespace
+
+namespace mi355attn {
+
+bool launch_log_on() {
+  // C++ initialises a function-local static once, even under concurrent first calls.
+  static const bool on = [] {
+    const char* e = getenv("MI355ATTN_LOG");
+    return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void launch_log(const char* fmt, ...) {
+  char line[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(line, sizeof line, fmt, ap);
+  va_end(ap);
+  fprintf(stderr, "mi355attn: %s\n", line);
+}
+
+}  // namespace mi355attn
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                         int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,

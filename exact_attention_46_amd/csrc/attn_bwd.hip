@@ -586,11 +586,16 @@ template <int DT, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // dQ first: it also writes D, which the dK/dV kernel reads.
   const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
+  MI355_LOG("attn_bwd_dq_kernel<%s,%d,%s> grid=%lld block=%d then attn_bwd_dkdv_kernel grid=%lld "
+            "block=%d B=%d Hq=%d Hkv=%d Nq=%d Nk=%d scale=%g delta=%p stream=%p",
+            dtype_name(DT), D, CAUSAL ? "causal" : "full", (long long)a.B * a.Hq * nqt,
+            kBwdThreads, (long long)a.B * a.Hkv * nkt, kDkdvThreads, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+            (double)a.scale, (void*)a.delta, (void*)stream);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt)),
                      dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
                      a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
-  const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
                      dim3(kDkdvThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,

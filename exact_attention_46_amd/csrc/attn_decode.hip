@@ -800,6 +800,11 @@ static hipError_t launch_split_t(const SplitArgs& a, hipStream_t stream) {
   const int C = (int)(((int64_t)max_len + a.chunk - 1) / a.chunk);
   const PagedKV pk{a.block_table, a.page_size, a.max_pages, a.num_pages};
   uint16_t* o_fin = (uint16_t*)a.o_final;
+  MI355_LOG("attn_decode_split_kernel<%s,%d,%s%s> grid=%d block=%d B=%d Hq=%d Hkv=%d max_len=%d "
+            "chunk=%d chunks=%d page_size=%d scale=%g stream=%p",
+            dtype_name(DT), D, a.block_table ? "paged" : "padded",
+            a.counters ? ",fused" : a.o_final ? ",one-pass" : "", device_cus(), kSplitThreads,
+            a.B, a.Hq, a.Hkv, max_len, a.chunk, C, a.page_size, (double)a.scale, (void*)stream);
 #define MI355_SPLIT_LAUNCH(P, FIN, FU)                                                           \
   hipLaunchKernelGGL((attn_decode_split_kernel<DT, D, P, FIN, FU>), dim3((unsigned)device_cus()), \
                      dim3(kSplitThreads), 0, stream, (const uint16_t*)a.q,                       \
@@ -826,6 +831,9 @@ template <int DT, int D>
 static hipError_t launch_combine_t(const CombineArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.B * a.Hq;
   const int64_t blocks = (rows + 3) / 4;
+  MI355_LOG("attn_decode_combine_kernel<%s,%d> grid=%lld block=256 B=%d Hq=%d chunks=%d chunk=%d "
+            "stream=%p",
+            dtype_name(DT), D, (long long)blocks, a.B, a.Hq, a.max_chunks, a.chunk, (void*)stream);
   hipLaunchKernelGGL((attn_decode_combine_kernel<DT, D>), dim3((unsigned)blocks), dim3(256), 0,
                      stream, a.part_o, a.part_lse, a.seq_lens, (uint16_t*)a.o, a.lse, a.B, a.Hq,
                      a.max_chunks, a.chunk);

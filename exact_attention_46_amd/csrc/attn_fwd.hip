@@ -757,7 +757,16 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const VarLen vl{a.cu_q, a.cu_k, a.total_q, a.total_k, a.q_stride, a.kv_stride, a.o_stride,
                   a.uniform_len};
   const Window win{a.window_left, a.window_right};
-  if (a.local && local_split(a.window_left, a.window_right)) {
+  const bool halves = a.local && local_split(a.window_left, a.window_right);
+  MI355_LOG("attn_fwd_kernel<%s,%d,%s> grid=%lld block=%d B=%d Hq=%d Hkv=%d Nq=%d Nk=%d "
+            "window=(%d,%d) total_q=%d total_k=%d scale=%g stream=%p",
+            dtype_name(DT), D,
+            halves ? "local,two-halves" : a.local ? "local" : a.cu_q ? (CAUSAL ? "causal,varlen" : "varlen")
+            : a.uniform_len > 0 ? (CAUSAL ? "causal,token-major" : "token-major")
+            : (CAUSAL ? "causal" : "full"),
+            (long long)blocks, kFwdThreads, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.window_left,
+            a.window_right, a.total_q, a.total_k, (double)a.scale, (void*)stream);
+  if (halves) {
     hipLaunchKernelGGL((attn_fwd_kernel<DT, D, false, false, true, true>), dim3((unsigned)blocks),
                        dim3(kFwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                        (const uint16_t*)a.v, (uint16_t*)a.o, a.lse, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,

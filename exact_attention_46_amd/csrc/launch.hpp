@@ -6,6 +6,19 @@
 
 namespace mi355attn {
 
+// Launch log. With MI355ATTN_LOG set in the environment to anything but "" or
+// "0", every kernel launch prints one line to stderr ("mi355attn: " then the
+// kernel, its grid and block and the problem's shape). The variable is read
+// once per process, at the first launch; logging never changes what runs.
+bool launch_log_on();
+void launch_log(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+#define MI355_LOG(...)                                              \
+  do {                                                              \
+    if (::mi355attn::launch_log_on()) ::mi355attn::launch_log(__VA_ARGS__); \
+  } while (0)
+
+inline const char* dtype_name(int dt) { return dt == 0 ? "bf16" : "fp16"; }
+
 struct FwdArgs {
   const void* q;
   const void* k;

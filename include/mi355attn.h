@@ -7,8 +7,14 @@
  *  - Tensors are dense, row-major, in device memory owned by the caller. The
  *    library allocates nothing, keeps no workspace and no mutable global state
  *    (apart from a per-device cache of the compute-unit count, which the split
- *    kernels size their grid by), and may be called from several host threads
- *    at once.
+ *    kernels size their grid by, the fixed device array of attn_bwd_noalloc
+ *    with its per-device address, and the launch-log switch below), and may be
+ *    called from several host threads at once.
+ *  - Launch log: with the environment variable MI355ATTN_LOG set to anything
+ *    but "" or "0" when the first kernel is launched, every launch prints one
+ *    line to stderr, "mi355attn: " then the kernel (dtype, head dim, variant),
+ *    its grid and block, the problem's shape and the stream. The variable is
+ *    read once per process; logging changes nothing that runs.
  *  - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *    Every call only enqueues work on that stream and returns at once.
  *  - The return value covers argument checks and the launch itself
