@@ -56,6 +56,8 @@ KERNEL_SOURCES = {
     "attn_decode_split_kernel": ["common.hpp", "attn_decode.hip"],
     "attn_bwd_dq_kernel": ["common.hpp", "attn_bwd.hip"],
     "attn_bwd_dkdv_kernel": ["common.hpp", "attn_bwd.hip"],
+    "attn_bwd_delta_kernel": ["common.hpp", "attn_bwd.hip"],
+    "attn_bwd_dq_ds_kernel": ["common.hpp", "attn_bwd.hip"],
 }
 
 
@@ -100,8 +102,8 @@ def parse():
 
 # Single measurements for counter runs (bench.py --only NAME): the forward on
 # another workload, the backward, the fused decode and its paged form.
-ONLY_EXTRA = ["fwd_gqa_prefill", "fwd_long_context", "bwd", "decode_fused", "decode_fused_paged",
-              "fwd_local"]
+ONLY_EXTRA = ["fwd_gqa_prefill", "fwd_long_context", "bwd", "bwd_ds", "decode_fused",
+              "decode_fused_paged", "fwd_local"]
 
 COPY_CAL_BYTES = 256 << 20  # bytes read (and written) by one calibration launch
 COPY_CAL_MATCH = "neg"      # the calibration kernel's name contains this
@@ -145,8 +147,11 @@ TRAFFIC_RUNS = {
     "fwd_gqa_prefill": [("attn_fwd_kernel/gqa_prefill", "attn_fwd_kernel")],
     "fwd_long_context": [("attn_fwd_kernel/long_context", "attn_fwd_kernel")],
     "fwd_local": [("attn_fwd_kernel/local", "attn_fwd_kernel<0, 128, false, false, true,")],
-    "bwd": [("attn_bwd_dq_kernel/llm_prefill", "attn_bwd_dq_kernel"),
-            ("attn_bwd_dkdv_kernel/llm_prefill", "attn_bwd_dkdv_kernel")],
+    "bwd": [("attn_bwd_dq_kernel/llm_prefill", "attn_bwd_dq_kernel<"),
+            ("attn_bwd_dkdv_kernel/llm_prefill", "attn_bwd_dkdv_kernel<0, 128, true, false>")],
+    "bwd_ds": [("attn_bwd_delta_kernel/llm_prefill", "attn_bwd_delta_kernel"),
+               ("attn_bwd_dkdv_kernel/llm_prefill_ds", "attn_bwd_dkdv_kernel<0, 128, true, true>"),
+               ("attn_bwd_dq_ds_kernel/llm_prefill", "attn_bwd_dq_ds_kernel")],
     "decode_fused": [("attn_decode_split_kernel/decode_fused",
                       "attn_decode_split_kernel<0, 128, false, false, true>")],
     "decode_fused_paged": [("attn_decode_split_kernel/decode_fused_paged",
@@ -379,19 +384,25 @@ def bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc, stream):
 VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX = 8192, 256, 4096
 
 
-def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
+def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream, stored_ds=False):
     """Backward on the llm_prefill workload (dO drawn like the inputs). TFLOP/s with
     the usual convention: 2.5x the forward's flops (five products of the forward's
-    size); the kernels perform seven (S and dP are recomputed by both the dK/dV
-    and the dQ kernels). Timed in a loop of its own after the steps."""
-    print("bench: backward", file=sys.stderr, flush=True)
+    size). attn_bwd performs seven (S and dP are recomputed by both the dK/dV and
+    the dQ kernels); stored_ds: attn_bwd_ds, which performs five and moves dS
+    through a workspace in HBM (a D kernel, dK/dV storing dS^T, dQ = dS K).
+    Timed in a loop of its own after the steps."""
+    print("bench: backward%s" % (" (stored dS)" if stored_ds else ""), file=sys.stderr, flush=True)
     g = torch.Generator(device="cpu").manual_seed(wp.seed + 100)
     do = torch.randn(qg.shape, generator=g).to(qg.dtype).to(qg.device)
     dq, dk, dv = torch.empty_like(qg), torch.empty_like(kg), torch.empty_like(vg)
     delta = torch.empty_like(lseg)
+    ds = ea.ds_workspace(qg, kg) if stored_ds else None
 
     def run():
-        ea.attn_bwd(qg, kg, vg, og, do, lseg, delta, dq, dk, dv, True, wp.scale, stream)
+        if stored_ds:
+            ea.attn_bwd_ds(qg, kg, vg, og, do, lseg, delta, ds, dq, dk, dv, True, wp.scale, stream)
+        else:
+            ea.attn_bwd(qg, kg, vg, og, do, lseg, delta, dq, dk, dv, True, wp.scale, stream)
 
     for _ in range(max(1, args.warmup)):
         run()
@@ -406,17 +417,25 @@ def bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream):
     ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
     flops = 2.5 * 4.0 * wp.B * wp.Hq * wp.N * wp.N * wp.d / 2.0
     tf = flops / (ms * 1e-3) / 1e12
-    return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
-            "flop_convention": "2.5 x forward (causal halved)",
-            "roofline": {"kernel": "attn_bwd (dq + dkdv kernels)", "bound": "mfma",
-                         "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": _bwd_traffic()}}
+    out = {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
+           "flop_convention": "2.5 x forward (causal halved)",
+           "roofline": {"kernel": ("attn_bwd_ds (delta + dkdv storing dS + dq from dS kernels)"
+                                   if stored_ds else "attn_bwd (dq + dkdv kernels)"),
+                        "bound": "mfma",
+                        "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": _bwd_traffic(stored_ds)}}
+    if stored_ds:
+        out["workspace_bytes"] = int(ds.numel())
+    return out
 
 
-def _bwd_traffic():
-    a = load_traffic("attn_bwd_dq_kernel/llm_prefill")
-    b = load_traffic("attn_bwd_dkdv_kernel/llm_prefill")
-    return a + b if a is not None and b is not None else None
+def _bwd_traffic(stored_ds=False):
+    names = (["attn_bwd_delta_kernel/llm_prefill", "attn_bwd_dkdv_kernel/llm_prefill_ds",
+              "attn_bwd_dq_ds_kernel/llm_prefill"] if stored_ds else
+             ["attn_bwd_dq_kernel/llm_prefill", "attn_bwd_dkdv_kernel/llm_prefill"])
+    vals = [load_traffic(n) for n in names]
+    return sum(vals) if all(v is not None for v in vals) else None
 
 
 LOCAL_WINDOW = 512
@@ -670,12 +689,13 @@ def run_only(args, torch, np, ea, wl, wp, wd, dev):
     name = args.only
     if name in ("fwd_gqa_prefill", "fwd_long_context"):
         return {name: bench_fwd_workload(args, torch, np, ea, wl, name[4:], dev, stream)}
-    if name in ("bwd", "fwd_local"):
+    if name in ("bwd", "bwd_ds", "fwd_local"):
         q, k, v = (t.to(dev) for t in wl.workload_prefill_inputs(wp))
         if name == "fwd_local":
             return {name: bench_local(args, torch, np, ea, wp, q, k, v, stream)}
         o, lse = ea.fwd(q, k, v, causal=True, scale=wp.scale)
-        return {name: bench_bwd(args, torch, np, ea, wp, q, k, v, o, lse, stream)}
+        return {name: bench_bwd(args, torch, np, ea, wp, q, k, v, o, lse, stream,
+                                stored_ds=(name == "bwd_ds"))}
     sl, dq, kc, vc = wl.workload_decode_inputs(wd, device=dev)
     dq, sld = dq.to(dev), sl.to(dev)
     return {name: bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream,
@@ -818,6 +838,8 @@ def main():
                                       "traffic": load_traffic("attn_decode_split_kernel/decode")}}
     if do_pre and not args.no_bwd:
         out["bwd"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream)
+        out["bwd_ds"] = bench_bwd(args, torch, np, ea, wp, qg, kg, vg, og, lseg, stream,
+                                  stored_ds=True)
     if do_pre and not args.no_local:
         out["fwd_local"] = bench_local(args, torch, np, ea, wp, qg, kg, vg, stream)
     if do_pre and not args.no_qkv:

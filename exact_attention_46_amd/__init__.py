@@ -13,6 +13,10 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     attn_bwd,
     attn_bwd_noalloc,
+    attn_bwd_ds,
+    attn_bwd_ds_workspace,
+    bwd_ds,
+    ds_workspace,
     attn_decode,
     attn_decode_combine,
     attn_decode_fused,

@@ -29,7 +29,7 @@ ERR_HIP = -6
 ERR_SCRATCH = -7
 
 EXPORTS = ("attn_fwd", "attn_fwd_varlen", "attn_fwd_local", "attn_fwd_qkvpacked", "attn_bwd",
-           "attn_bwd_noalloc",
+           "attn_bwd_noalloc", "attn_bwd_ds", "attn_bwd_ds_workspace",
            "attn_decode_split",
            "attn_decode_split_paged", "attn_decode_combine", "attn_decode",
            "attn_decode_workspace", "attn_decode_fused", "attn_decode_fused_paged",
@@ -55,13 +55,16 @@ def load_library() -> ctypes.CDLL:
                                "exact_attention_46_amd.build); there is no fallback")
         lib = ctypes.CDLL(LIB_PATH)
         p, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        ll = ctypes.c_longlong
         lib.attn_fwd.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_varlen.argtypes = [p, p, p, p, p, p, p, i, i, i, i, i, i, i, f, i, i, p]
         lib.attn_fwd_local.argtypes = [p, p, p, p, p, i, i, i, i, i, i, f, i, i, i, p]
         lib.attn_fwd_qkvpacked.argtypes = [p, p, p, i, i, i, i, f, i, i, p]
         lib.attn_bwd.argtypes = [p, p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
         lib.attn_bwd_noalloc.argtypes = [p, p, p, p, p, p, p, p, p, i, i, i, i, i, i, f, i, i, p]
-        ll = ctypes.c_longlong
+        lib.attn_bwd_ds.argtypes = [p, p, p, p, p, p, p, p, ll, p, p, p, i, i, i, i, i, i, f, i, i,
+                                    p]
+        lib.attn_bwd_ds_workspace.argtypes = [i, i, i, i]
         lib.attn_decode.argtypes = [p, p, p, p, p, p, p, ll, i, i, i, i, i, f, i, p]
         lib.attn_decode_workspace.argtypes = [i, i, i, i, i]
         lib.attn_decode_split.argtypes = [p, p, p, p, p, p, i, i, i, i, i, i, f, i, p]
@@ -79,6 +82,8 @@ def load_library() -> ctypes.CDLL:
         lib.attn_fwd_qkvpacked.restype = i
         lib.attn_bwd.restype = i
         lib.attn_bwd_noalloc.restype = i
+        lib.attn_bwd_ds.restype = i
+        lib.attn_bwd_ds_workspace.restype = ctypes.c_longlong
         lib.attn_decode.restype = i
         lib.attn_decode_workspace.restype = ctypes.c_longlong
         lib.attn_decode_split.restype = i
@@ -241,6 +246,60 @@ def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: flo
                                          _stream(stream))
     if st != OK:
         raise AttnError("attn_bwd_noalloc", st)
+
+
+def attn_bwd_ds_workspace(B: int, Hq: int, Nq: int, Nk: int) -> int:
+    """Bytes of the dS^T workspace attn_bwd_ds needs (raises on a bad shape)."""
+    n = load_library().attn_bwd_ds_workspace(B, Hq, Nq, Nk)
+    if n < 0:
+        raise AttnError("attn_bwd_ds_workspace", int(n))
+    return int(n)
+
+
+def ds_workspace(q, k) -> torch.Tensor:
+    """A dS^T workspace for attn_bwd_ds (uninitialised bytes; 256-byte aligned)."""
+    B, Hq, Nq, _ = q.shape
+    n = attn_bwd_ds_workspace(B, Hq, Nq, k.shape[2])
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def attn_bwd_ds(q, k, v, o, dout, lse, delta, ds, dq, dk, dv, causal: bool, scale: float,
+                stream=None) -> None:
+    """Calls attn_bwd_ds: attn_bwd with dS stored once in the workspace `ds` (a uint8
+    tensor of at least attn_bwd_ds_workspace bytes) instead of recomputed."""
+    _gpu(q, k, v, o, dout, lse, delta, ds, dq, dk, dv)
+    _need(q.dim() == 4 and k.dim() == 4 and v.shape == k.shape, "q, k, v must be 4-D, k ~ v")
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    _need(k.shape[0] == B and k.shape[3] == d, "k/v batch or head dim differ from q")
+    for t in (k, v, o, dout, dq, dk, dv):
+        _need(t.dtype == q.dtype, "dtypes differ")
+    _need(o.shape == q.shape and dout.shape == q.shape and dq.shape == q.shape,
+          "o, dout, dq must have q's shape")
+    _need(dk.shape == k.shape and dv.shape == k.shape, "dk, dv must have k's shape")
+    for t in (lse, delta):
+        _need(t.dtype == torch.float32 and tuple(t.shape) == (B, Hq, Nq), "lse/delta [B,Hq,Nq] fp32")
+    _need(ds.is_contiguous(), "ds must be contiguous")
+    st = load_library().attn_bwd_ds(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                    _ptr(delta), _ptr(ds), ds.numel() * ds.element_size(),
+                                    _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, Nq, Nk, d,
+                                    float(scale), int(bool(causal)), _dtype_code(q),
+                                    _stream(stream))
+    if st != OK:
+        raise AttnError("attn_bwd_ds", st)
+
+
+def bwd_ds(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None,
+           stream=None, ds=None):
+    """Allocates (unless `ds` is given) and returns (dq, dk, dv) through attn_bwd_ds."""
+    if scale is None:
+        scale = default_scale(q.shape[-1])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if ds is None:
+        ds = ds_workspace(q, k)
+    attn_bwd_ds(q, k, v, o, dout, lse, delta, ds, dq, dk, dv, causal, scale, stream)
+    return dq, dk, dv
 
 
 def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, stream=None):

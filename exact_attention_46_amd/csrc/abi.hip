@@ -143,6 +143,44 @@ extern "C" int attn_bwd(const void* q, const void* k, const void* v, const void*
   return from_hip(mi355attn::launch_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+
+// Bytes of the stored dS^T for attn_bwd_ds (-1 when the shape is out of range).
+int64_t bwd_ds_bytes(int B, int Hq, int Nq, int Nk) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0 || Nk <= 0 || Nq > kMaxSeq || Nk > kMaxSeq) return -1;
+  const int64_t per_head = mi355attn::bwd_ds_bytes_per_head(Nq, Nk);
+  if (per_head > (INT64_MAX / 2) / ((int64_t)B * Hq)) return -1;
+  return (int64_t)B * Hq * per_head;
+}
+
+}  // namespace
+
+extern "C" long long attn_bwd_ds_workspace(int B, int Hq, int Nq, int Nk) {
+  const int64_t n = bwd_ds_bytes(B, Hq, Nq, Nk);
+  return n < 0 ? (long long)MI355ATTN_ERR_BAD_SHAPE : (long long)n;
+}
+
+extern "C" int attn_bwd_ds(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, float* delta, void* ds,
+                           long long ds_bytes, void* dq, void* dk, void* dv, int B, int Hq,
+                           int Hkv, int Nq, int Nk, int d, float scale, int causal, int dtype,
+                           void* stream) {
+  if (!delta || !ds) return MI355ATTN_ERR_NULL_PTR;
+  const int st = bwd_status(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                            causal, dtype);
+  if (st != MI355ATTN_OK) return st;
+  if (!aligned(delta, 4) || !aligned(ds, 256)) return MI355ATTN_ERR_MISALIGNED;
+  const int64_t need = bwd_ds_bytes(B, Hq, Nq, Nk);
+  if (need < 0) return MI355ATTN_ERR_BAD_SHAPE;
+  if (ds_bytes < need) return MI355ATTN_ERR_BAD_ARG;
+  if (mi355attn::bwd_ds_grid_blocks(B, Hq, Nq) > kMaxGrid) return MI355ATTN_ERR_BAD_SHAPE;
+  mi355attn::BwdArgs a{q, k, v, o, dout, lse, delta, dq, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale,
+                       causal, dtype};
+  a.ds = ds;
+  a.ds_row_blocks = (int)mi355attn::bwd_ds_row_blocks(Nq);
+  return from_hip(mi355attn::launch_bwd_ds(a, static_cast<hipStream_t>(stream)));
+}
+
 extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
                                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
                                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,

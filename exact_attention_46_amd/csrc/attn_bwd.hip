@@ -170,13 +170,30 @@ __device__ __forceinline__ void lds_exchange_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int DT, int D, bool CAUSAL>
+// Stored dS^T (attn_bwd_ds): blocks of kDsKeys keys x kDsRows query rows, one
+// per (batch * Hq + head, 128-row block, 64-key tile) in that order, each
+// kDsBlock bytes contiguous, key-major inside (a key's 128 rows are 256
+// contiguous bytes); the dQ kernel streams the key tiles of its row blocks.
+constexpr int kDsKeys = 64;
+constexpr int kDsRows = 128;
+constexpr int kDsBlock = kDsKeys * kDsRows * 2;
+static_assert(kDsRows == kBwdRowsWG && kDsKeys == kBwdKT && kBwdKeysWG % kDsKeys == 0 &&
+                  kDsRows % kBwdQT == 0,
+              "a dK/dV wave's step and a dQ tile each fall in one block");
+
+// STORE_DS: the second role also stores its dS (rounded to the input dtype) to
+// ds_t in the blocked layout above (ds_row_blocks = ceil(Nq / kDsRows)), for
+// attn_bwd_dq_ds_kernel. Every (key, row) pair with the key allowed for the row
+// is written (rows >= Nq and keys >= Nk of a block as zeros); pairs of rows the
+// workgroup's steps do not reach are causally masked and left as they were.
+template <int DT, int D, bool CAUSAL, bool STORE_DS = false>
 __global__ void __launch_bounds__(kDkdvThreads, 2)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                      const float* __restrict__ lse, const float* __restrict__ delta,
                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int B, int Hq, int Hkv,
-                     int Nq, int Nk, float scale) {
+                     int Nq, int Nk, float scale, uint16_t* __restrict__ ds_t,
+                     int ds_row_blocks) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdQT * ROW;
   constexpr int STAGE = 2 * TILE + 2 * kBwdQT * 4;  // Q, dO, LSE, D
@@ -254,6 +271,18 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   auto begin_step = [&](int i) {
     wait_all_memory();
     __syncthreads();
+    if (i + 1 < n_steps) issue(i + 1);
+  };
+  // The same for the second role when it stores dS: its 4 stores of step i-1
+  // were issued after the loads of step i and may stay in flight (completion
+  // is in order, so vmcnt <= 4 means those loads have landed); a bare barrier,
+  // since __syncthreads would wait for the stores too.
+  auto begin_step_st = [&](int i) {
+    wait_vmcnt_lgkmcnt0<4>();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
     if (i + 1 < n_steps) issue(i + 1);
   };
   // Whether any (row, key) pair of step i and this wave's keys is masked:
@@ -342,7 +371,20 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       const unsigned char* tq = smem + BUF * STAGE;
       const unsigned char* tdo = tq + TILE;
       const float* sdl = (const float*)(tq + 2 * TILE) + kBwdQT;
-      (void)i;
+      // The dS^T block of this wave's keys and the step's rows (a wave whose
+      // keys all lie past Nk has no block: its resource is empty).
+      __amdgpu_buffer_rsrc_t rds;
+      uint32_t ds_lane = 0;
+      if constexpr (STORE_DS) {
+        const int h = g * group + i / per_head;
+        const int r0 = (t_begin + i % per_head) * kBwdQT;
+        const int nkb = (Nk + kDsKeys - 1) / kDsKeys;
+        const int64_t blk = (((int64_t)b * Hq + h) * ds_row_blocks + r0 / kDsRows) * nkb + kw0 / kDsKeys;
+        rds = make_rsrc(ds_t + blk * (kDsBlock / 2), kw0 < Nk ? (uint32_t)kDsBlock : 0u);
+        ds_lane = (uint32_t)((kw0 % kDsKeys + r32) * kDsRows + r0 % kDsRows + 8 * half) * 2u;
+      } else {
+        (void)i;
+      }
       f32x16_t dp[2];
 #pragma unroll
       for (int rb = 0; rb < kBwdQT / 32; ++rb) {
@@ -378,6 +420,20 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                              pack2<DT>(dsv[8 * ks + 2], dsv[8 * ks + 3]),
                              pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
                              pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
+        if constexpr (STORE_DS) {
+          // sf[ks] holds rows 32rb + 16ks + 8j + 4half + 0..3 in words 2j, 2j+1.
+          // Swapping the j = 1 pieces of the low half with the j = 0 pieces of
+          // the high half leaves rows 32rb + 16ks + 8half + 0..7 in each lane:
+          // one 16-byte store.
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const auto w0 = __builtin_amdgcn_permlane32_swap(sf[ks][0], sf[ks][2], false, false);
+            const auto w1 = __builtin_amdgcn_permlane32_swap(sf[ks][1], sf[ks][3], false, false);
+            __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){w0[0], w1[0], w0[1], w1[1]}, rds,
+                                                   ds_lane + (uint32_t)(32 * rb + 16 * ks) * 2u,
+                                                   0, 0);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
@@ -387,10 +443,10 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int i = 0; i < n_steps; i += 2) {
-      begin_step(i);
+      if constexpr (STORE_DS) begin_step_st(i); else begin_step(i);
       step(std::integral_constant<int, 0>{}, i);
       if (i + 1 < n_steps) {
-        begin_step(i + 1);
+        if constexpr (STORE_DS) begin_step_st(i + 1); else begin_step(i + 1);
         step(std::integral_constant<int, 1>{}, i + 1);
       }
     }
@@ -574,6 +630,202 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- dQ from a stored dS
+
+// D_i = sum_t dO_it O_it for every row of [rows, D] tensors: each row is summed
+// by the D/8 lanes that load its 16-byte chunks, then reduced across them.
+// Workgroups of 4 waves take 64 rows (16 per wave).
+constexpr int kDeltaRowsWG = 64;
+
+template <int DT, int D>
+__global__ void __launch_bounds__(256)
+attn_bwd_delta_kernel(const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout,
+                      float* __restrict__ delta, int64_t rows) {
+  constexpr int CH = D / 8, RPL = 64 / CH, LOADS = 16 / RPL;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t r_wave = (int64_t)blockIdx.x * kDeltaRowsWG + wave * 16;
+  const int c = lane % CH;
+  u32x4_t ov[LOADS], dv[LOADS];
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    const int64_t row = r_wave + i * RPL + lane / CH;
+    ov[i] = dv[i] = (u32x4_t){0u, 0u, 0u, 0u};
+    if (row < rows) {
+      ov[i] = *reinterpret_cast<const u32x4_t*>(o + row * D + c * 8);
+      dv[i] = *reinterpret_cast<const u32x4_t*>(dout + row * D + c * 8);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = dot2_acc<DT>(ov[i][j], dv[i][j], acc);
+#pragma unroll
+    for (int m = CH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+    const int64_t row = r_wave + i * RPL + lane / CH;
+    if (row < rows && c == 0) delta[row] = acc;
+  }
+}
+
+// Stages ROWS rows of 128 16-bit values, row r at src + r * stride_bytes (rows
+// >= rows_valid read as zero), into an LDS tile laid out like the K tiles of
+// width 128 (chunk index XOR bwd_swz<128>).
+template <int ROWS, int NW>
+__device__ __forceinline__ void stage_rows128_strided(const uint16_t* src, uint32_t stride_bytes,
+                                                      int rows_valid, unsigned char* tile,
+                                                      int tid) {
+  constexpr int CH = 16, RPL = 64 / CH, LOADS = ROWS / RPL;
+  static_assert(LOADS % NW == 0, "loads split evenly over the waves");
+  const int wave = tid >> 6, lane = tid & 63;
+  const int rv = min(rows_valid, ROWS);
+  const auto rs = make_rsrc(src, rv > 0 ? (uint32_t)(rv - 1) * stride_bytes + 256u : 0u);
+#pragma unroll
+  for (int i = 0; i < LOADS / NW; ++i) {
+    const int ld = wave * (LOADS / NW) + i;
+    const int row = ld * RPL + lane / CH;
+    const int pc = lane % CH;
+    buf_load16_lds(rs, tile + ld * 1024,
+                   (uint32_t)row * stride_bytes + (uint32_t)((pc ^ bwd_swz<128>(row)) << 4));
+  }
+}
+
+// dQ = scale * dS K from the dS^T that attn_bwd_dkdv_kernel<..., true> stored:
+// one workgroup of 8 waves per 256 query rows of one (batch, head), each wave 32
+// rows, walking 64-key tiles of K and of dS^T (the two stored blocks of the
+// workgroup's rows: 64 keys x 128 rows, 16 KiB contiguous each) staged in LDS
+// three buffers deep, so that two tiles are in flight while one is used (the
+// kernel is bound by reading dS). Both operands of dQ^T += K^T dS^T come from
+// transposing reads (lane: d index or query row; k-slots: keys), with no
+// recomputation of S or dP. On tiles that straddle a wave's causal diagonal the
+// dS^T operand is masked to zero past each row's last key (entries the dK/dV
+// kernel did not write lie only there).
+constexpr int kDqDsWaves = 8;
+constexpr int kDqDsRows = 32 * kDqDsWaves;
+constexpr int kDqDsThreads = 64 * kDqDsWaves;
+constexpr int kDqDsStages = 3;
+static_assert(kDqDsRows == 2 * kDsRows, "two stored blocks per tile");
+
+template <int DT, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kDqDsThreads, 1)
+attn_bwd_dq_ds_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ ds_t,
+                      uint16_t* __restrict__ dq, int B, int Hq, int Hkv, int Nq, int Nk,
+                      int ds_row_blocks, float scale) {
+  constexpr int DB = D / 32, ROW = D * 2;
+  constexpr int KTILE = kBwdKT * ROW;
+  constexpr int STAGE = KTILE + 2 * kDsBlock;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kDqDsStages * STAGE];
+  static_assert(kDqDsStages * STAGE <= 160 * 1024, "LDS of a gfx950 workgroup");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r32 = lane & 31, half = lane >> 5;
+  const int nqt = (Nq + kDqDsRows - 1) / kDqDsRows;
+  int unit, qt;
+  bwd_block_of(blockIdx.x, B * Hq, nqt, unit, qt);
+  if (CAUSAL) qt = nqt - 1 - qt;
+  const int b = unit / Hq, h = unit % Hq;
+  const int g = h / (Hq / Hkv);
+  const int off = Nk - Nq;
+  const int q0 = qt * kDqDsRows;
+  const int qw0 = q0 + 32 * wave;
+  const int my_row = qw0 + r32;
+  const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
+  const int nkb = (Nk + kDsKeys - 1) / kDsKeys;
+  // The workgroup's first stored block (row block 2 * qt, key tile 0); key tile
+  // t is t blocks on, the second row block nkb blocks on.
+  const uint16_t* dsh = ds_t + (((int64_t)unit * ds_row_blocks + 2 * qt) * nkb) * (kDsBlock / 2);
+  const bool second_block = 2 * qt + 1 < ds_row_blocks;
+
+  f32x16_t dqa[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dqa[db] = (f32x16_t){};
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kDqDsRows, Nq) - 1 + off + 1));
+  const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
+  // Loads per wave per tile: K's 1 KiB loads spread over the 8 waves, and 4 of
+  // one dS^T block (waves 0-3 the first block, 4-7 the second; an absent second
+  // block reads as zeros), so the wait for a tile is a fixed count.
+  constexpr int KLOADS = kBwdKT / (64 / (D / 8)) / kDqDsWaves;
+  constexpr int TILE_LOADS = KLOADS + kBwdKT / 4 / (kDqDsWaves / 2);
+  static_assert(KLOADS >= 1 && TILE_LOADS == KLOADS + 4, "load split");
+  auto issue = [&](int t) {
+    unsigned char* st = smem + (t % kDqDsStages) * STAGE;
+    stage_rows<D, kBwdKT, kDqDsWaves>(k + kvoff, t * kBwdKT, Nk, st, tid);
+    const int blk = wave >> 2;
+    const uint16_t* src = dsh + ((int64_t)blk * nkb + t) * (kDsBlock / 2);
+    const int keys = (blk == 1 && !second_block) ? 0 : Nk - t * kBwdKT;
+    stage_rows128_strided<kBwdKT, kDqDsWaves / 2>(src, (uint32_t)kDsRows * 2u, keys,
+                                                  st + KTILE + blk * kDsBlock, tid & 255);
+  };
+  auto step = [&](auto buf_c, int t) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const int k0 = t * kBwdKT;
+    if (CAUSAL && k0 > qw0 + 31 + off) return;
+    const bool masked = CAUSAL && k0 + kBwdKT - 1 > qw0 + off;
+    const unsigned char* tk = smem + BUF * STAGE;
+    const unsigned char* tds = tk + KTILE + (wave >> 2) * kDsBlock;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      // lane: query row r32 of this wave; slot m: key k0 + 16ks + 8(m/4) + 4half + m%4
+      u32x4_t sb = tile_tr<128>(tds, ks, wave & 3, lane);
+      if (masked) {
+        const int lim = my_row + off - (k0 + 16 * ks + 4 * half);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int o_lo = 8 * (w >> 1) + 2 * (w & 1);  // key offset of slot 2w
+          const uint32_t keep = (o_lo <= lim ? 0x0000ffffu : 0u) | (o_lo + 1 <= lim ? 0xffff0000u : 0u);
+          sb[w] &= keep;
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sb, dqa[db]);
+    }
+  };
+  // Start of tile t: this wave's loads of tile t have landed (those of tile
+  // t + 1, issued later, may not have); the barrier publishes every wave's and
+  // ends all reads of tile t - 1, whose buffer tile t + 2 then takes.
+  auto begin_tile = [&](int t) {
+    if (t + 1 < n_tiles)
+      wait_vmcnt_lgkmcnt0<TILE_LOADS>();
+    else
+      wait_all_memory();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 2 < n_tiles) issue(t + 2);
+  };
+  if (n_tiles > 0) issue(0);
+  if (n_tiles > 1) issue(1);
+  for (int t = 0; t < n_tiles; t += kDqDsStages) {
+    begin_tile(t);
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) {
+      begin_tile(t + 1);
+      step(std::integral_constant<int, 1>{}, t + 1);
+    }
+    if (t + 2 < n_tiles) {
+      begin_tile(t + 2);
+      step(std::integral_constant<int, 2>{}, t + 2);
+    }
+  }
+
+  if (my_row < Nq) {
+    uint16_t* pq = dq + (((int64_t)b * Hq + h) * (int64_t)Nq + my_row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d0 = 32 * db + 8 * gq + 4 * half;
+        *reinterpret_cast<u32x2_t*>(pq + d0) =
+            (u32x2_t){pack2<DT>(dqa[db][4 * gq + 0] * scale, dqa[db][4 * gq + 1] * scale),
+                      pack2<DT>(dqa[db][4 * gq + 2] * scale, dqa[db][4 * gq + 3] * scale)};
+      }
+  }
+}
+
 // ---------------------------------------------------------------- launch
 
 int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk) {
@@ -599,7 +851,8 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
                      dim3(kDkdvThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
-                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale,
+                     nullptr, 0);
   return hipGetLastError();
 }
 
@@ -634,6 +887,57 @@ static hipError_t bwd_scratch(float** out) {
   }
   *out = p;
   return hipSuccess;
+}
+
+int64_t bwd_ds_row_blocks(int Nq) { return ((int64_t)Nq + kDsRows - 1) / kDsRows; }
+
+int64_t bwd_ds_bytes_per_head(int Nq, int Nk) {
+  return ((int64_t)Nk + kDsKeys - 1) / kDsKeys * bwd_ds_row_blocks(Nq) * kDsBlock;
+}
+
+int64_t bwd_ds_grid_blocks(int B, int Hq, int Nq) {
+  return ((int64_t)B * Hq * Nq + kDeltaRowsWG - 1) / kDeltaRowsWG;
+}
+
+template <int DT, int D, bool CAUSAL>
+static hipError_t launch_bwd_ds_t(const BwdArgs& a, hipStream_t stream) {
+  // D first, then dK/dV (which reads D and stores dS^T), then dQ from dS^T.
+  const int64_t rows = (int64_t)a.B * a.Hq * a.Nq;
+  const int nqt2 = (a.Nq + kDqDsRows - 1) / kDqDsRows;
+  const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
+  MI355_LOG("attn_bwd_delta_kernel<%s,%d> grid=%lld block=256, attn_bwd_dkdv_kernel<%s,%d,%s,ds> "
+            "grid=%lld block=%d, attn_bwd_dq_ds_kernel grid=%lld block=%d B=%d Hq=%d Hkv=%d "
+            "Nq=%d Nk=%d ds_row_blocks=%d scale=%g stream=%p",
+            dtype_name(DT), D, (long long)bwd_ds_grid_blocks(a.B, a.Hq, a.Nq), dtype_name(DT), D,
+            CAUSAL ? "causal" : "full", (long long)a.B * a.Hkv * nkt, kDkdvThreads,
+            (long long)a.B * a.Hq * nqt2, kDqDsThreads, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.ds_row_blocks,
+            (double)a.scale, (void*)stream);
+  hipLaunchKernelGGL((attn_bwd_delta_kernel<DT, D>),
+                     dim3((unsigned)bwd_ds_grid_blocks(a.B, a.Hq, a.Nq)), dim3(256), 0, stream,
+                     (const uint16_t*)a.o, (const uint16_t*)a.dout, a.delta, rows);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL, true>), dim3((unsigned)(a.B * a.Hkv * nkt)),
+                     dim3(kDkdvThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, (const uint16_t*)a.dout, a.lse, a.delta,
+                     (uint16_t*)a.dk, (uint16_t*)a.dv, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale,
+                     (uint16_t*)a.ds, a.ds_row_blocks);
+  hipLaunchKernelGGL((attn_bwd_dq_ds_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt2)),
+                     dim3(kDqDsThreads), 0, stream, (const uint16_t*)a.k, (const uint16_t*)a.ds,
+                     (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.ds_row_blocks, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_ds(const BwdArgs& a, hipStream_t stream) {
+#define MI355_BWD_DS_CASE(DTV, DV)                                              \
+  if (a.dtype == DTV && a.d == DV) {                                            \
+    return a.causal ? launch_bwd_ds_t<DTV, DV, true>(a, stream)                 \
+                    : launch_bwd_ds_t<DTV, DV, false>(a, stream);               \
+  }
+  MI355_BWD_DS_CASE(kBF16, 128)
+  MI355_BWD_DS_CASE(kBF16, 64)
+  MI355_BWD_DS_CASE(kFP16, 128)
+  MI355_BWD_DS_CASE(kFP16, 64)
+#undef MI355_BWD_DS_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_bwd_noalloc(const BwdArgs& args, hipStream_t stream) {

@@ -227,6 +227,14 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
   __builtin_amdgcn_sched_barrier(0);
 }
+// Wait until at most N vector memory operations and no LDS operation of this
+// wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkmcnt0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_sched_barrier(0);
+}
 // Wait until every LDS operation of this wave has completed.
 __device__ __forceinline__ void wait_lgkmcnt0() {
   __builtin_amdgcn_s_waitcnt(0xc07f);

@@ -93,6 +93,10 @@ struct BwdArgs {
   float scale;
   int causal;
   int dtype;
+  // attn_bwd_ds: the stored dS^T in blocks of 64 keys x 128 rows
+  // (ds_row_blocks = bwd_ds_row_blocks(Nq)).
+  void* ds = nullptr;
+  int ds_row_blocks = 0;
 };
 
 // Number of workgroups the forward launch uses (for the grid-size check).
@@ -113,6 +117,11 @@ constexpr int64_t kBwdScratchFloats = int64_t(1) << 22;
 hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 // launch_bwd with a.delta replaced by the fixed scratch of the current device.
+hipError_t launch_bwd_ds(const BwdArgs& a, hipStream_t stream);
+// Row blocks of the stored dS^T and its bytes per (batch, head).
+int64_t bwd_ds_row_blocks(int Nq);
+int64_t bwd_ds_bytes_per_head(int Nq, int Nk);
+int64_t bwd_ds_grid_blocks(int B, int Hq, int Nq);
 hipError_t launch_bwd_noalloc(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_split(const SplitArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);

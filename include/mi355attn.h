@@ -143,6 +143,35 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              int Nq, int Nk, int d, float scale, int causal, int dtype, void* stream);
 
 /*
+ * attn_bwd_ds — attn_bwd with the score gradient dS stored once instead of
+ * recomputed (the llm.c page's attention_backward keeps the whole score
+ * gradient matrix in memory; here it is written once, rounded to dtype, and
+ * read once): D from dout and o, then dk and dv (which also write dS^T to `ds`),
+ * then dq = scale * dS k from `ds`, so S and dP are formed once per (row, key)
+ * pair instead of twice.
+ *
+ *   arguments as attn_bwd, plus
+ *   ds        workspace owned by the caller, 256-byte aligned, ds_bytes long,
+ *             at least attn_bwd_ds_workspace(B, Hq, Nq, Nk) bytes (written,
+ *             then read; its contents on entry do not matter)
+ *
+ * The workspace holds dS^T in blocks of 64 keys x 128 query rows (16 KiB each,
+ * one per (batch, head, 64-key tile, 128-row block)): B * Hq * ceil(Nk / 64) *
+ * ceil(Nq / 128) * 16384 bytes (1 GiB at B=4, Hq=32, Nq=Nk=2048), so this form
+ * suits moderate lengths; attn_bwd needs no such buffer. Three kernels run in order on `stream`; no atomics. ds_bytes below
+ * the requirement returns MI355ATTN_ERR_BAD_ARG, a misaligned ds
+ * MI355ATTN_ERR_MISALIGNED.
+ */
+int attn_bwd_ds(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, float* delta, void* ds, long long ds_bytes, void* dq,
+                void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                int causal, int dtype, void* stream);
+
+/* Bytes attn_bwd_ds needs in `ds` (MI355ATTN_ERR_BAD_SHAPE for sizes <= 0 or
+ * lengths above 2^23). */
+long long attn_bwd_ds_workspace(int B, int Hq, int Nq, int Nk);
+
+/*
  * attn_bwd_noalloc — attn_bwd for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * it): the same kernels and the same result, with D kept in a fixed scratch

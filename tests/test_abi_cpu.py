@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 A = ctypes.c_void_p(4096)   # aligned, non-NULL stand-ins: never dereferenced,
 A2 = ctypes.c_void_p(8192)  # every call below fails validation first
 MIS = ctypes.c_void_p(4098)
+A16 = ctypes.c_void_p(4096 + 16)  # 16-byte but not 256-byte aligned
 
 
 def declared_functions():
@@ -122,6 +123,35 @@ def bwd_noalloc(lib, q=A, k=A, v=A, o=A, do=A, lse=A2, dq=A, dk=A, dv=A, B=1, Hq
 ])
 def test_attn_bwd_noalloc_rejects(lib, kw, code):
     assert bwd_noalloc(lib, **kw) == code
+
+
+def bwd_ds(lib, q=A, k=A, v=A, o=A, do=A, lse=A2, delta=A2, ds=A, ds_bytes=1 << 20, dq=A,
+           dk=A, dv=A, B=1, Hq=2, Hkv=2, Nq=8, Nk=8, d=128, scale=0.1, causal=1, dtype=0):
+    return lib.attn_bwd_ds(q, k, v, o, do, lse, delta, ds, ds_bytes, dq, dk, dv, B, Hq, Hkv, Nq,
+                           Nk, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1), (dict(delta=None), -1), (dict(ds=None), -1),
+    (dict(B=0), -2), (dict(Hq=3, Hkv=2), -2), (dict(Nk=2**23 + 1), -2),
+    (dict(d=32), -3), (dict(dtype=4), -3),
+    (dict(scale=float("nan")), -5), (dict(causal=-1), -5),
+    (dict(ds=A16), -4), (dict(delta=MIS), -4),
+    # the workspace must hold B * Hq * ceil(Nk / 64) * ceil(Nq / 128) blocks of 16 KiB
+    (dict(ds_bytes=2 * 16384 - 1), -5), (dict(ds_bytes=0), -5),
+])
+def test_attn_bwd_ds_rejects(lib, kw, code):
+    assert bwd_ds(lib, **kw) == code
+
+
+def test_attn_bwd_ds_workspace_sizes(lib):
+    # B * Hq * ceil(Nk / 64) * ceil(Nq / 128) blocks of 64 x 128 values of 2 bytes
+    n = lib.attn_bwd_ds_workspace(1, 2, 8, 8)
+    assert n == 2 * 16384
+    assert lib.attn_bwd_ds_workspace(4, 32, 2048, 2048) == 4 * 32 * 2048 * 2048 * 2
+    assert lib.attn_bwd_ds_workspace(1, 1, 129, 65) == 2 * 2 * 16384
+    assert lib.attn_bwd_ds_workspace(0, 1, 1, 1) == -2
+    assert lib.attn_bwd_ds_workspace(1, 1, 2**23 + 1, 1) == -2
 
 
 def fwd_varlen(lib, q=A, k=A, v=A, o=A2, lse=A2, cq=A, ck=A2, B=3, Hq=4, Hkv=2, total_q=100,

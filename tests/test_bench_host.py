@@ -34,7 +34,10 @@ FWD = "void mi355attn::attn_fwd_kernel<0, 128, true, false, false>(unsigned shor
 DEC = "void mi355attn::attn_decode_split_kernel<0, 128, false, false, false>(unsigned short const*)"
 PAG = "void mi355attn::attn_decode_split_kernel<0, 128, true, false, false>(unsigned short const*)"
 DQ = "void mi355attn::attn_bwd_dq_kernel<0, 128, true>(unsigned short const*)"
-DKDV = "void mi355attn::attn_bwd_dkdv_kernel<0, 128, true>(unsigned short const*)"
+DKDV = "void mi355attn::attn_bwd_dkdv_kernel<0, 128, true, false>(unsigned short const*)"
+DELTA = "void mi355attn::attn_bwd_delta_kernel<0, 128>(unsigned short const*)"
+DKDV_DS = "void mi355attn::attn_bwd_dkdv_kernel<0, 128, true, true>(unsigned short const*)"
+DQ_DS = "void mi355attn::attn_bwd_dq_ds_kernel<0, 128, true>(unsigned short const*)"
 CAL = "void at::native::vectorized_elementwise_kernel<neg_kernel>(int)"
 
 
@@ -71,6 +74,15 @@ def test_record_traffic_scales_by_the_calibration_kernel(tmp_path, monkeypatch):
     rec = json.loads(out.read_text())
     assert rec["attn_bwd_dq_kernel/llm_prefill"]["bytes_per_launch"] == 10 * 1024 + 1024
     assert "attn_decode_split_kernel/decode" in rec and "bwd" in rec["_calibration"]
+    assert bench._bwd_traffic() == 10 * 1024 + 1024 + 20 * 1024 + 2 * 1024
+    # the stored-dS backward: three kernels, the dK/dV one told apart by its template
+    assert bench._bwd_traffic(stored_ds=True) is None
+    _write_counters(tmp_path / "f3", "FETCH_SIZE",
+                    [(CAL, kib), (DELTA, 3.0), (DKDV_DS, 30.0), (DQ_DS, 40.0)])
+    _write_counters(tmp_path / "w3", "WRITE_SIZE",
+                    [(CAL, kib), (DELTA, 0.5), (DKDV_DS, 50.0), (DQ_DS, 4.0)])
+    bench.record_traffic(str(tmp_path / "f3"), str(tmp_path / "w3"), "bwd_ds")
+    assert bench._bwd_traffic(stored_ds=True) == (3 + 30 + 40) * 1024 + (0.5 + 50 + 4) * 1024
     assert bench._bwd_traffic() == 10 * 1024 + 1024 + 20 * 1024 + 2 * 1024
 
 

@@ -727,6 +727,74 @@ def test_backward_full_size_sampled_heads():
         _check_grad(sl(dv.cpu()), rv, bv, w.dtype, tag + " dv")
 
 
+# --------------------------------------------------------------- backward through a stored dS
+
+BWD_DS = BWD + [
+    # Nq != Nk with causal alignment: the dK/dV workgroups leave dS^T entries of
+    # rows above their first step unwritten; the dQ kernel must mask them
+    (1, 4, 2, 200, 500, 128, "bf16", True),
+    (1, 4, 4, 500, 200, 64, "fp16", True),
+    (2, 4, 4, 130, 70, 128, "bf16", True),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", BWD_DS)
+def test_backward_ds(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    """attn_bwd_ds against the oracle (the same per-element bound as attn_bwd), with
+    the dS workspace filled with NaN bit patterns first, so that a read of an entry
+    the dK/dV kernel did not write would show."""
+    seed = zlib.crc32(repr(("bwd", B, Hq, Hkv, Nq, Nk, d, dtype, causal)).encode()) % 10000
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = ea.fwd(qd, kd, vd, causal=causal, scale=scale)
+    outs = [_guarded(t.shape, t.dtype) for t in (qd, kd, vd)]
+    deltab, delta = _guarded(tuple(lse.shape), torch.float32)
+    n = ea.attn_bwd_ds_workspace(B, Hq, Nq, Nk)
+    assert n == B * Hq * ((Nk + 63) // 64) * ((Nq + 127) // 128) * 16384
+    ds = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    ea.attn_bwd_ds(qd, kd, vd, o, dod, lse, delta, ds, outs[0][1], outs[1][1], outs[2][1],
+                   causal, scale)
+    torch.cuda.synchronize()
+    for buf, t in outs + [(deltab, delta)]:
+        assert _guard_ok(buf, t.numel()), "write outside an output"
+    rq, rk, rv = oracle.attn_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do),
+                                 wl.DTYPE_CODE[dtype], scale, causal)
+    bq, bk, bv = grad_bound(q, k, v, do, dtype, scale, causal)
+    tag = "bwd_ds %s" % ((B, Hq, Hkv, Nq, Nk, d, dtype, causal),)
+    _check_grad(outs[0][1], rq, bq, dtype, tag + " dq")
+    _check_grad(outs[1][1], rk, bk, dtype, tag + " dk")
+    _check_grad(outs[2][1], rv, bv, dtype, tag + " dv")
+    if causal and Nq > Nk:
+        assert not outs[0][1][:, :, : Nq - Nk].any(), "rows with no key must get dq = 0"
+
+
+def test_backward_ds_full_size_sampled_heads():
+    """attn_bwd_ds on the whole llm_prefill workload (as the benchmark runs it), three
+    (batch, head) slices against the oracle's backward of that head alone."""
+    w = wl.WORKLOADS["llm_prefill"]
+    q, k, v = wl.workload_prefill_inputs(w)
+    g = torch.Generator().manual_seed(w.seed + 7)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = ea.fwd(qd, kd, vd, causal=True, scale=w.scale)
+    dq, dk, dv = ea.bwd_ds(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 1)
+    picks = [(0, 0), (w.B - 1, w.Hq - 1), (int(rng.integers(w.B)), int(rng.integers(w.Hq)))]
+    for b, h in picks:
+        sl = lambda t: t[b:b + 1, h:h + 1].contiguous()
+        rq, rk, rv = oracle.attn_bwd(wl.bits(sl(q)), wl.bits(sl(k)), wl.bits(sl(v)),
+                                     wl.bits(sl(do)), wl.DTYPE_CODE[w.dtype], w.scale, True)
+        bq, bk, bv = grad_bound(sl(q), sl(k), sl(v), sl(do), w.dtype, w.scale, True)
+        tag = "bwd_ds llm_prefill b=%d h=%d" % (b, h)
+        _check_grad(sl(dq.cpu()), rq, bq, w.dtype, tag + " dq")
+        _check_grad(sl(dk.cpu()), rk, bk, w.dtype, tag + " dk")
+        _check_grad(sl(dv.cpu()), rv, bv, w.dtype, tag + " dv")
+
+
 # --------------------------------------------------------------- one-call decode (library chunk)
 
 AUTO = [
