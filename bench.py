@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
     "attn_bwd_dkdv_kernel": ["common.hpp", "attn_bwd.hip"],
     "attn_bwd_delta_kernel": ["common.hpp", "attn_bwd.hip"],
     "attn_bwd_dq_ds_kernel": ["common.hpp", "attn_bwd.hip"],
+    "attn_decode_combine_kernel": ["common.hpp", "attn_decode.hip"],
 }
 
 
@@ -103,7 +104,7 @@ def parse():
 # Single measurements for counter runs (bench.py --only NAME): the forward on
 # another workload, the backward, the fused decode and its paged form.
 ONLY_EXTRA = ["fwd_gqa_prefill", "fwd_long_context", "bwd", "bwd_ds", "decode_fused",
-              "decode_fused_paged", "fwd_local"]
+              "decode_fused_paged", "fwd_local", "fwd_qkvpacked", "fwd_varlen", "decode_auto"]
 
 COPY_CAL_BYTES = 256 << 20  # bytes read (and written) by one calibration launch
 COPY_CAL_MATCH = "neg"      # the calibration kernel's name contains this
@@ -156,6 +157,11 @@ TRAFFIC_RUNS = {
                       "attn_decode_split_kernel<0, 128, false, false, true>")],
     "decode_fused_paged": [("attn_decode_split_kernel/decode_fused_paged",
                             "attn_decode_split_kernel<0, 128, true, false, true>")],
+    "fwd_qkvpacked": [("attn_fwd_kernel/qkvpacked", "attn_fwd_kernel")],
+    "fwd_varlen": [("attn_fwd_kernel/varlen", "attn_fwd_kernel")],
+    "decode_auto": [("attn_decode_split_kernel/decode_auto",
+                     "attn_decode_split_kernel<0, 128, false, false, false>"),
+                    ("attn_decode_combine_kernel/decode_auto", "attn_decode_combine_kernel")],
 }
 
 
@@ -380,7 +386,16 @@ def bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc, stream):
             "chunk_slots": slots, "chunk": -(-kc.shape[2] // slots), "workspace_floats": n,
             "roofline": {"kernel": "attn_decode_split_kernel + combine (library chunk)",
                          "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None}}
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": _sum_traffic(["attn_decode_split_kernel/decode_auto",
+                                                  "attn_decode_combine_kernel/decode_auto"])}}
+
+
+def _sum_traffic(names):
+    vals = [load_traffic(n) for n in names]
+    return sum(vals) if all(v is not None for v in vals) else None
+
+
 VARLEN_TOKENS, VARLEN_MIN, VARLEN_MAX = 8192, 256, 4096
 
 
@@ -534,7 +549,8 @@ def bench_qkvpacked(args, torch, np, ea, wp, stream):
     return {"value": round(tf, 2), "unit": "TFLOP/s", "ms": round(ms, 4),
             "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal,token-major>", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("attn_fwd_kernel/qkvpacked")}}
 
 
 def bench_varlen(args, torch, np, ea, wl, dev, stream):
@@ -569,7 +585,8 @@ def bench_varlen(args, torch, np, ea, wl, dev, stream):
             "seq_lens": lens,
             "roofline": {"kernel": "attn_fwd_kernel<bf16,128,causal,varlen>", "bound": "mfma",
                          "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None}}
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                         "traffic": load_traffic("attn_fwd_kernel/varlen")}}
 
 
 def bench_paged(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream):
@@ -689,6 +706,10 @@ def run_only(args, torch, np, ea, wl, wp, wd, dev):
     name = args.only
     if name in ("fwd_gqa_prefill", "fwd_long_context"):
         return {name: bench_fwd_workload(args, torch, np, ea, wl, name[4:], dev, stream)}
+    if name == "fwd_qkvpacked":
+        return {name: bench_qkvpacked(args, torch, np, ea, wp, stream)}
+    if name == "fwd_varlen":
+        return {name: bench_varlen(args, torch, np, ea, wl, dev, stream)}
     if name in ("bwd", "bwd_ds", "fwd_local"):
         q, k, v = (t.to(dev) for t in wl.workload_prefill_inputs(wp))
         if name == "fwd_local":
@@ -698,6 +719,8 @@ def run_only(args, torch, np, ea, wl, wp, wd, dev):
                                 stored_ds=(name == "bwd_ds"))}
     sl, dq, kc, vc = wl.workload_decode_inputs(wd, device=dev)
     dq, sld = dq.to(dev), sl.to(dev)
+    if name == "decode_auto":
+        return {name: bench_decode_auto(args, torch, np, ea, wd, sl, dq, sld, kc, vc, stream)}
     return {name: bench_decode_fused(args, torch, np, ea, wl, wd, sl, dq, sld, kc, vc, stream,
                                      paged=(name == "decode_fused_paged"))}
 
