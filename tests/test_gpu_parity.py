@@ -925,3 +925,51 @@ def test_fwd_qkvpacked(B, N, H, d, dtype, causal):
     torch.cuda.synchronize()
     assert torch.equal(od.transpose(1, 2).contiguous().view(torch.int16), o.view(torch.int16))
     assert torch.equal(ld, lse)
+
+
+# --------------------------------------------------------------- maximum lengths
+
+MAX_SEQ = 1 << 23  # the longest sequence the C ABI accepts
+
+
+def test_fwd_maximum_key_length():
+    """Nk at the ABI's limit: one head's K and V are 2 GiB each, so its per-head byte
+    offsets reach 2^31. 192 causal rows aligned to the bottom-right corner (the last
+    row sees every key), four rows checked against the oracle."""
+    Nq, Nk, d = 192, MAX_SEQ, 128
+    g = torch.Generator(device="cuda").manual_seed(1234)
+    q = torch.randn((1, 1, Nq, d), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, 1, Nk, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, 1, Nk, d), generator=g, device="cuda").to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_fwd(q, k, v, True, scale)
+    rows = np.array([[0, 0, 0], [0, 0, 1], [0, 0, 100], [0, 0, Nq - 1]], dtype=np.int64)
+    ro, rl = oracle.attn_fwd_rows(wl.bits(q.cpu()), wl.bits(k.cpu()), wl.bits(v.cpu()), 0,
+                                  scale, True, rows)
+    check(o[0, 0, rows[:, 2]], lse[0, 0, rows[:, 2]], ro, rl, "bf16",
+          "forward, Nk = 2^23 (rows 0, 1, 100, 191)")
+
+
+def test_decode_maximum_length():
+    """One sequence of 2^23 keys (the ABI's limit: 2 GiB of K and of V for its
+    kv-head) through the split + combine (16384 chunks of 512 keys), the one-call and
+    the fused decode, each against the oracle."""
+    Hq, Hkv, d = 4, 1, 128
+    g = torch.Generator(device="cuda").manual_seed(4321)
+    q = torch.randn((1, Hq, d), generator=g, device="cuda").to(torch.bfloat16)
+    kc = torch.randn((1, Hkv, MAX_SEQ, d), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((1, Hkv, MAX_SEQ, d), generator=g, device="cuda").to(torch.bfloat16)
+    sl = torch.tensor([MAX_SEQ], dtype=torch.int32)
+    sld = sl.cuda()
+    scale = 1.0 / math.sqrt(d)
+    ro, rl = oracle.decode(wl.bits(q.cpu()), wl.bits(kc.cpu()), wl.bits(vc.cpu()), sl.numpy(),
+                           0, scale)
+    o, lse = ea.decode(q, kc, vc, sld, chunk=512, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, ro, rl, "bf16", "split + combine decode, L = 2^23")
+    o, lse = ea.decode_auto(q, kc, vc, sld, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, ro, rl, "bf16", "one-call decode, L = 2^23")
+    o, lse = ea.decode_fused(q, kc, vc, sld, chunk=512, scale=scale)
+    torch.cuda.synchronize()
+    check(o, lse, ro, rl, "bf16", "fused decode, L = 2^23")
