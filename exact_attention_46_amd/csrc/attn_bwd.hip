@@ -275,10 +275,14 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   };
   // The same for the second role when it stores dS: its 4 stores of step i-1
   // were issued after the loads of step i and may stay in flight (completion
-  // is in order, so vmcnt <= 4 means those loads have landed); a bare barrier,
-  // since __syncthreads would wait for the stores too.
+  // is in order, so vmcnt <= 4 means those loads have landed; before step 0
+  // no store was issued, so there every operation is waited for); a bare
+  // barrier, since __syncthreads would wait for the stores too.
   auto begin_step_st = [&](int i) {
-    wait_vmcnt_lgkmcnt0<4>();
+    if (i == 0)
+      wait_all_memory();
+    else
+      wait_vmcnt_lgkmcnt0<4>();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
