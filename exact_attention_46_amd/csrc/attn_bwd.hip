@@ -158,17 +158,38 @@ __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float acc) {
 
 // ---------------------------------------------------------------- dK, dV
 
-// Barrier between the two halves of a dK/dV step: the P values that the
-// first-role waves stored to LDS are complete and visible to the second-role
-// waves. Only LDS operations are waited for (the next stage's global loads stay
-// in flight), and the compiler fences keep memory accesses on their side.
-__device__ __forceinline__ void lds_exchange_barrier() {
+// Barriers of a dK/dV iteration. phase_barrier<VM>: the wave first waits until
+// at most VM of its vector-memory operations are outstanding (the newest ones:
+// completion is in order, so everything issued before them has landed) and
+// for all of its LDS operations; the barrier then publishes the stage loads
+// and the LDS stores of every wave. lds_barrier waits for this wave's LDS
+// operations only; bare_barrier waits for nothing (each wave has consumed what
+// it read). The compiler fences keep memory accesses on their side.
+template <int VM>
+__device__ __forceinline__ void phase_barrier() {
+  wait_vmcnt_lgkmcnt0<VM>();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void lds_barrier() {
   wait_lgkmcnt0();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_barrier();
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_sched_barrier(0);
 }
+__device__ __forceinline__ void bare_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
 
 // Stored dS^T (attn_bwd_ds): blocks of kDsKeys keys x kDsRows query rows, one
 // per (batch * Hq + head, 128-row block, 64-key tile) in that order, each
@@ -186,6 +207,20 @@ static_assert(kDsRows == kBwdRowsWG && kDsKeys == kBwdKT && kBwdKeysWG % kDsKeys
 // attn_bwd_dq_ds_kernel. Every (key, row) pair with the key allowed for the row
 // is written (rows >= Nq and keys >= Nk of a block as zeros); pairs of rows the
 // workgroup's steps do not reach are causally masked and left as they were.
+//
+// Schedule. Step j is one 64-row tile of Q and dO (with its LSE and D) in LDS
+// ring slot j % 3. Iteration j has two phases, and in each the two waves of a
+// SIMD take opposite roles, one issuing matrix products while the other runs
+// element-wise work (as in the forward):
+//   phase 1: first role  P(j) = exp(scale S(j) - LSE) -> exchange buffer
+//            second role dK^T += Q(j-1)^T dS(j-1), dP(j) = dO(j) V^T
+//   phase 2: first role  dV^T += dO(j)^T P(j), S(j+1) = Q(j+1) K^T
+//            second role dS(j) = P(j) (dP(j) - D)
+// After the barrier between the phases each wave issues its part of stage
+// j+2's loads (into the slot of step j-1, whose last reader was dK(j-1)); they
+// have the next two phases to land and are waited for at the next iteration's
+// phase barrier. The first-role S(0) runs before iteration 0, and iteration
+// n_steps only finishes dK.
 template <int DT, int D, bool CAUSAL, bool STORE_DS = false>
 __global__ void __launch_bounds__(kDkdvThreads, 2)
 attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -196,18 +231,31 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
                      int ds_row_blocks) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdQT * ROW;
-  constexpr int STAGE = 2 * TILE + 2 * kBwdQT * 4;  // Q, dO, LSE, D
   constexpr int XCHG = kBwdKeysWG * kBwdQT * 4;     // P of one step (fp32)
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE + XCHG];
-  float* const xchg = reinterpret_cast<float*>(smem + 2 * STAGE);
+  // LDS: the P exchange, the LSE and D rows of three ring slots, then the Q
+  // tiles and the dO tiles of the three slots. The exchange and the rows are
+  // addressed with immediate offsets (which reach 64 KiB), the tiles through
+  // per-lane bases (below).
+  constexpr int XCHG_AT = 0, LD_AT = XCHG;
+  constexpr int Q_AT = LD_AT + ((3 * 2 * kBwdQT * 4 + 1023) / 1024) * 1024;
+  constexpr int DO_AT = Q_AT + 3 * TILE;
+  // Loads per second-role wave of one stage (the second-role waves issue all
+  // of them, in their element-wise phase): Q and dO rows; waves 4 and 5 also
+  // load LSE / D.
+  constexpr int ROW_LOADS = kBwdQT / (64 / (D / 8)) / (kDkdvWaves / 2);
+  static_assert(ROW_LOADS >= 1 && DO_AT + 3 * TILE <= 160 * 1024, "stage ring of a gfx950 workgroup");
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[DO_AT + 3 * TILE];
+  float* const xchg = reinterpret_cast<float*>(smem + XCHG_AT);
+  auto q_tile = [&](int sl) { return smem + Q_AT + sl * TILE; };
+  auto do_tile = [&](int sl) { return smem + DO_AT + sl * TILE; };
+  auto lse_rows = [&](int sl) { return reinterpret_cast<float*>(smem + LD_AT) + sl * 2 * kBwdQT; };
+  auto d_rows = [&](int sl) { return lse_rows(sl) + kBwdQT; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // Waves kb and kb + 4 (which share a SIMD) own the same 32 keys. The first
-  // computes S = Q K^T, P and dV; the second dP = dO V^T, dS = P (dP - D) and
-  // dK, taking P from the first through LDS. Each holds one of K, V and one of
-  // the two accumulators, and while one issues its products the other can run
-  // its element-wise work.
+  // keeps their K rows and computes S, P and dV; the second keeps their V rows
+  // and computes dP, dS (with the first's P, through LDS) and dK.
   const int kb = wave & 3;
   const bool second = wave >= 4;
   const int r32 = lane & 31, half = lane >> 5;
@@ -238,6 +286,11 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   f32x16_t acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) acc[db] = (f32x16_t){};
+  // S (first role) or dP (second role) of a step: 64 rows x 32 keys in two
+  // 32-row blocks, one key per lane; and P (first role) or dS (second role)
+  // packed to 16 bits in the B-operand layout of the dV / dK products.
+  f32x16_t sp[2];
+  u32x4_t pk[2][2];
   const float c = scale * kLog2e;
   // This lane's P values of row block rb in the exchange buffer: four 16-byte
   // pieces, each piece of the 64 lanes contiguous.
@@ -252,207 +305,306 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   const int t_end = (Nq + kBwdQT - 1) / kBwdQT;
   const int per_head = max(0, t_end - t_begin);
   const int n_steps = group * per_head;
-  // Stage loads of step i into buffer i & 1: Q and dO rows (all waves), LSE
-  // (wave 0) and D (wave 1).
-  auto issue = [&](int i) {
+  auto step_row0 = [&](int i) { return (t_begin + i % per_head) * kBwdQT; };
+  // Stage of step i into ring slot SL (== i % 3), issued by the second-role
+  // waves: Q and dO rows, LSE (wave 4) and D (wave 5).
+  auto issue = [&](auto slot_c, int i) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
     const int h = g * group + i / per_head;
-    const int r0 = (t_begin + i % per_head) * kBwdQT;
+    const int r0 = step_row0(i);
     const int64_t qoff = ((int64_t)b * Hq + h) * (int64_t)Nq;
-    unsigned char* st = smem + (i & 1) * STAGE;
-    stage_rows<D, kBwdQT, kDkdvWaves>(q + qoff * D, r0, Nq, st, tid);
-    stage_rows<D, kBwdQT, kDkdvWaves>(dout + qoff * D, r0, Nq, st + TILE, tid);
-    if (wave == 0) stage_floats64(lse + qoff, r0, Nq, (float*)(st + 2 * TILE), lane);
-    if (wave == 1) stage_floats64(delta + qoff, r0, Nq, (float*)(st + 2 * TILE) + kBwdQT, lane);
+    const int rtid = tid - 64 * (kDkdvWaves / 2);  // thread index within the role
+    stage_rows<D, kBwdQT, kDkdvWaves / 2>(q + qoff * D, r0, Nq, q_tile(SL), rtid);
+    stage_rows<D, kBwdQT, kDkdvWaves / 2>(dout + qoff * D, r0, Nq, do_tile(SL), rtid);
+    if (wave == 4) stage_floats64(lse + qoff, r0, Nq, lse_rows(SL), lane);
+    if (wave == 5) stage_floats64(delta + qoff, r0, Nq, d_rows(SL), lane);
   };
-  if (n_steps > 0) issue(0);
-  // Start of step i: its loads (this wave's) have landed; the barrier
-  // publishes every wave's and also ends all reads of step i-1 (its stage,
-  // whose buffer the loads of step i+1 reuse, and the exchange buffer).
-  auto begin_step = [&](int i) {
-    wait_all_memory();
-    __syncthreads();
-    if (i + 1 < n_steps) issue(i + 1);
+  // The LSE rows of a stage, scaled in place to -LSE * log2(e) (the exponent
+  // offset of P = exp2(scale log2(e) S - LSE log2(e))) by wave 4 once they have
+  // landed, so that P takes one multiply-add per element.
+  auto scale_lse = [&](int sl) {
+    float* l = lse_rows(sl) + lane;
+    *l = -*l * kLog2e;
   };
-  // The same for the second role when it stores dS: its 4 stores of step i-1
-  // were issued after the loads of step i and may stay in flight (completion
-  // is in order, so vmcnt <= 4 means those loads have landed; before step 0
-  // no store was issued, so there every operation is waited for); a bare
-  // barrier, since __syncthreads would wait for the stores too.
-  auto begin_step_st = [&](int i) {
-    if (i == 0)
-      wait_all_memory();
-    else
-      wait_vmcnt_lgkmcnt0<4>();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_sched_barrier(0);
-    if (i + 1 < n_steps) issue(i + 1);
-  };
-  // Whether any (row, key) pair of step i and this wave's keys is masked:
-  // rows past Nq, keys past Nk, or (causal) a key after some row's diagonal.
+  // Whether any (row, key) pair of the step at r0 and this wave's keys is
+  // masked: rows past Nq, keys past Nk, or (causal) a key after some row's
+  // diagonal.
   auto needs_mask = [&](int r0) {
     return r0 + kBwdQT > Nq || kw0 + 32 > Nk || (CAUSAL && kw0 + 31 > r0 + off);
   };
-  // Each role runs its own copy of the step loop, and each step is compiled
-  // for both stage buffers, so every LDS address is a per-lane base set up
-  // once plus an immediate offset.
-  if (!second) {
-    // S = Q K^T for the step's 64 rows x 32 keys, P = exp(scale S - LSE) (0
-    // where masked), stored for the partner and kept packed for dV^T += dO^T P.
-    auto step = [&](auto buf_c, int i) {
-      constexpr int BUF = decltype(buf_c)::value;
-      const int r0 = (t_begin + i % per_head) * kBwdQT;
-      const bool masked = needs_mask(r0);
-      const unsigned char* tq = smem + BUF * STAGE;
-      const unsigned char* tdo = tq + TILE;
-      const float* slse = (const float*)(tq + 2 * TILE);
-      u32x4_t pf[2][2];
+
+  // Per-lane LDS byte addresses of the operand reads, each including the base
+  // of the kind of tile it reads (the first role reads Q as rows and dO
+  // transposed, the second the reverse); a ring slot, row block or k-step adds
+  // a compile-time offset below 64 KiB, which the reads take as their
+  // immediate. The empty asm keeps the compiler from folding those offsets
+  // into the addresses (which would need a register per slot).
+  // rows: row r32 (+32 rb) at logical chunk half*DS + ds;
+  // transposed: rows 4half + kk (+8 for the second read) at columns
+  // 32db + 16((lane >> 4) & 1) + 4a (as tile_tr).
+  uint32_t row_a[DS], tr_a[DB][2];
+  {
+    const uint32_t base = lds_addr(smem);
+    const uint32_t fam_rows = base + (second ? DO_AT : Q_AT);
+    const uint32_t fam_tr = base + (second ? Q_AT : DO_AT);
 #pragma unroll
-      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
-        u32x4_t qa[DS];
+    for (int ds = 0; ds < DS; ++ds) {
+      row_a[ds] = fam_rows + (uint32_t)(r32 * ROW + (((half * DS + ds) ^ bwd_swz<D>(r32)) << 4));
+      asm volatile("" : "+v"(row_a[ds]));
+    }
+    const int kk = (lane & 15) >> 2, a4 = lane & 3;
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) qa[ds] = tile_row16<D>(tq, 32 * rb + r32, half * DS + ds);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16_t sacc = (f32x16_t){};
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds) sacc = mfma32x32x16<DT>(qa[ds], bf[ds], sacc);
-        float p[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          // this lane's rows 32rb + 8gq + 4half + 0..3
-          const int lr = 32 * rb + 8 * gq + 4 * half;
-          const f32x4_t l4 = *reinterpret_cast<const f32x4_t*>(slse + lr);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int e = 4 * gq + x;
-            p[e] = fast_exp2(__builtin_fmaf(sacc[e], c, -l4[x] * kLog2e));
-          }
-          if (masked) {
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const int row = r0 + lr + x;
-              const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
-              p[4 * gq + x] = ok ? p[4 * gq + x] : 0.f;
-            }
-          }
-          *xchg_at(rb, gq) = (f32x4_t){p[4 * gq], p[4 * gq + 1], p[4 * gq + 2], p[4 * gq + 3]};
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          pf[rb][ks] = (u32x4_t){pack2<DT>(p[8 * ks + 0], p[8 * ks + 1]), pack2<DT>(p[8 * ks + 2], p[8 * ks + 3]),
-                                 pack2<DT>(p[8 * ks + 4], p[8 * ks + 5]), pack2<DT>(p[8 * ks + 6], p[8 * ks + 7])};
+      for (int w = 0; w < 2; ++w) {
+        const int r = 4 * half + kk + 8 * w;
+        const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * a4;
+        tr_a[db][w] = fam_tr + (uint32_t)(r * ROW + (((col >> 3) ^ bwd_swz<D>(r)) << 4) + (col & 7) * 2);
+        asm volatile("" : "+v"(tr_a[db][w]));
       }
-      lds_exchange_barrier();
-#pragma unroll
-      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
-        u32x4_t ta[2 * DB];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) ta[ks * DB + db] = tile_tr<D>(tdo, 2 * rb + ks, db, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(ta[ks * DB + db], pf[rb][ks], acc[db]);
+  }
+
+  // One matrix phase: N1 products into acc (block db = n / 4, k-step n % 4 =
+  // 2 rb + ks: A = the transposed tile in slot TRS, B = pk[rb][ks]), then N2
+  // products into sp (block rb = m / DS, step ds = m % DS: A = rows of the
+  // tile in slot RWS, B = bf[ds]). Each accumulator block is one dependent
+  // chain; A operands are read RA products ahead.
+  auto chain = [&](auto n1_c, auto n2_c, auto trs_c, auto rws_c) __attribute__((always_inline)) {
+    constexpr int N1 = decltype(n1_c)::value, N2 = decltype(n2_c)::value, NP = N1 + N2;
+    constexpr uint32_t TRS = decltype(trs_c)::value * TILE, RWS = decltype(rws_c)::value * TILE;
+    constexpr int RA = 4;
+    u32x4_t ring[RA];
+    auto read_a = [&](int n) {
+      if (n < N1) {
+        const int db = n / 4, kstep = n % 4;
+        const uint32_t o = TRS + (uint32_t)(16 * kstep * ROW);
+        const u32x2_t lo = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[db][0] + o));
+        const u32x2_t hi = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[db][1] + o));
+        ring[n % RA] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+      } else {
+        const int m = n - N1, rb = m / DS, ds = m % DS;
+        ring[n % RA] = lds_read16_staged(lds_ptr<const lds_u32x4_t>(row_a[ds] + RWS + (uint32_t)(32 * rb * ROW)));
       }
-      __builtin_amdgcn_sched_barrier(0);
     };
-    for (int i = 0; i < n_steps; i += 2) {
-      begin_step(i);
-      step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < n_steps) {
-        begin_step(i + 1);
-        step(std::integral_constant<int, 1>{}, i + 1);
+#pragma unroll
+    for (int n = 0; n < RA && n < NP; ++n) read_a(n);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int n = 0; n < NP; ++n) {
+      if (n < N1) {
+        const int db = n / 4, rb = (n % 4) / 2, ks = n % 2;
+        acc[db] = mfma32x32x16<DT>(ring[n % RA], pk[rb][ks], acc[db]);
+      } else {
+        const int m = n - N1, rb = m / DS, ds = m % DS;
+        sp[rb] = mfma32x32x16<DT>(ring[n % RA], bf[ds], ds == 0 ? (f32x16_t){} : sp[rb]);
+      }
+      if (n + RA < NP) read_a(n + RA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // First role, phase 1: P(j) = exp(scale S(j) - LSE) (0 where masked) from
+  // sp, stored for the partner and packed into pk for dV. All LDS reads of the
+  // phase go out first and the exchange stores last: interleaved, each group
+  // of rows would wait for a whole LDS round trip (the stores and the reads
+  // share the wait counter).
+  auto make_p = [&](auto slot_c, int j) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const int r0 = step_row0(j);
+    const bool masked = needs_mask(r0);
+    const float* slse = lse_rows(SL);
+    // this lane's rows 32rb + 8gq + 4half + 0..3
+    f32x4_t l4[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        l4[rb][gq] = *reinterpret_cast<const f32x4_t*>(slse + 32 * rb + 8 * gq + 4 * half);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sp[rb][e] = fast_exp2(__builtin_fmaf(sp[rb][e], c, l4[rb][e / 4][e % 4]));
+    if (masked) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = r0 + 32 * rb + 8 * (e / 4) + 4 * half + e % 4;
+          const bool ok = row < Nq && my_key < Nk && (!CAUSAL || my_key <= row + off);
+          sp[rb][e] = ok ? sp[rb][e] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        *xchg_at(rb, gq) = (f32x4_t){sp[rb][4 * gq], sp[rb][4 * gq + 1], sp[rb][4 * gq + 2], sp[rb][4 * gq + 3]};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pk[rb][ks] = (u32x4_t){pack2<DT>(sp[rb][8 * ks + 0], sp[rb][8 * ks + 1]), pack2<DT>(sp[rb][8 * ks + 2], sp[rb][8 * ks + 3]),
+                               pack2<DT>(sp[rb][8 * ks + 4], sp[rb][8 * ks + 5]), pack2<DT>(sp[rb][8 * ks + 6], sp[rb][8 * ks + 7])};
+    }
+  };
+
+  // Second role, phase 2: dS(j) = P(j) (dP(j) - D) with the partner's P (same
+  // lane and slot layout as dP) into pk for dK (and, STORE_DS, to ds_t). The
+  // P and D reads of a row block go out together before its arithmetic.
+  auto make_ds = [&](auto slot_c, int j) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    const float* sdl = d_rows(SL);
+    // The dS^T block of this wave's keys and the step's rows (a wave whose
+    // keys all lie past Nk has no block: its resource is empty).
+    __amdgpu_buffer_rsrc_t rds;
+    uint32_t ds_lane = 0;
+    if constexpr (STORE_DS) {
+      const int h = g * group + j / per_head;
+      const int r0 = step_row0(j);
+      const int nkb = (Nk + kDsKeys - 1) / kDsKeys;
+      const int64_t blk = (((int64_t)b * Hq + h) * ds_row_blocks + r0 / kDsRows) * nkb + kw0 / kDsKeys;
+      rds = make_rsrc(ds_t + blk * (kDsBlock / 2), kw0 < Nk ? (uint32_t)kDsBlock : 0u);
+      ds_lane = (uint32_t)((kw0 % kDsKeys + r32) * kDsRows + r0 % kDsRows + 8 * half) * 2u;
+    } else {
+      (void)j;
+    }
+#pragma unroll
+    for (int rb = 0; rb < kBwdQT / 32; ++rb) {
+      f32x4_t d4[4], p4[4];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        d4[gq] = *reinterpret_cast<const f32x4_t*>(sdl + 32 * rb + 8 * gq + 4 * half);
+        p4[gq] = *xchg_at(rb, gq);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sp[rb][e] = p4[e / 4][e % 4] * (sp[rb][e] - d4[e / 4][e % 4]);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        pk[rb][ks] = (u32x4_t){pack2<DT>(sp[rb][8 * ks + 0], sp[rb][8 * ks + 1]),
+                               pack2<DT>(sp[rb][8 * ks + 2], sp[rb][8 * ks + 3]),
+                               pack2<DT>(sp[rb][8 * ks + 4], sp[rb][8 * ks + 5]),
+                               pack2<DT>(sp[rb][8 * ks + 6], sp[rb][8 * ks + 7])};
+      if constexpr (STORE_DS) {
+        // pk[rb][ks] holds rows 32rb + 16ks + 8j + 4half + 0..3 in words 2j,
+        // 2j+1. Swapping the j = 1 pieces of the low half with the j = 0
+        // pieces of the high half leaves rows 32rb + 16ks + 8half + 0..7 in
+        // each lane: one 16-byte store.
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const auto w0 = __builtin_amdgcn_permlane32_swap(pk[rb][ks][0], pk[rb][ks][2], false, false);
+          const auto w1 = __builtin_amdgcn_permlane32_swap(pk[rb][ks][1], pk[rb][ks][3], false, false);
+          __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){w0[0], w1[0], w0[1], w1[1]}, rds,
+                                                 ds_lane + (uint32_t)(32 * rb + 16 * ks) * 2u, 0,
+                                                 0);
+        }
       }
     }
-  } else {
-    // dP = dO V^T for the step's 64 rows x 32 keys; dS = P (dP - D) with the
-    // partner's P (same lane and slot layout as dP), then dK^T += Q^T dS.
-    auto step = [&](auto buf_c, int i) {
-      constexpr int BUF = decltype(buf_c)::value;
-      const unsigned char* tq = smem + BUF * STAGE;
-      const unsigned char* tdo = tq + TILE;
-      const float* sdl = (const float*)(tq + 2 * TILE) + kBwdQT;
-      // The dS^T block of this wave's keys and the step's rows (a wave whose
-      // keys all lie past Nk has no block: its resource is empty).
-      __amdgpu_buffer_rsrc_t rds;
-      uint32_t ds_lane = 0;
-      if constexpr (STORE_DS) {
-        const int h = g * group + i / per_head;
-        const int r0 = (t_begin + i % per_head) * kBwdQT;
-        const int nkb = (Nk + kDsKeys - 1) / kDsKeys;
-        const int64_t blk = (((int64_t)b * Hq + h) * ds_row_blocks + r0 / kDsRows) * nkb + kw0 / kDsKeys;
-        rds = make_rsrc(ds_t + blk * (kDsBlock / 2), kw0 < Nk ? (uint32_t)kDsBlock : 0u);
-        ds_lane = (uint32_t)((kw0 % kDsKeys + r32) * kDsRows + r0 % kDsRows + 8 * half) * 2u;
-      } else {
-        (void)i;
+  };
+  // Stores of make_ds per step: they follow the next stage's loads in issue
+  // order and may stay in flight across the next phase barrier.
+  constexpr int DS_STORES = STORE_DS ? 2 * (kBwdQT / 32) : 0;
+
+  // Iteration j of each role (SL == j % 3); both roles pass the same two
+  // barriers. The steady-state iterations (FULL) take both products of their
+  // matrix phase; the first and last iterations of a role take one, and are
+  // compiled apart from the hot loop so that its register assignment is one.
+  // First role: FULL for j < n_steps - 1 (dV(j) and S(j+1)); j = n_steps - 1
+  // takes dV only, j = n_steps only passes the barriers.
+  auto iter_first = [&](auto slot_c, int j, auto full_c) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int NX = (SL + 1) % 3, PV = (SL + 2) % 3;
+    make_p(slot_c, j);
+    phase_barrier<0>();  // the exchange stores are complete
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (decltype(full_c)::value)
+      chain(ic<4 * DB>{}, ic<2 * DS>{}, ic<SL>{}, ic<NX>{});
+    else
+      chain(ic<4 * DB>{}, ic<0>{}, ic<SL>{}, ic<NX>{});
+    __builtin_amdgcn_s_setprio(0);
+    bare_barrier();
+  };
+  // Second role: j = 0 takes dP(0) only, FULL for 0 < j < n_steps (dK(j-1)
+  // and dP(j)), j = n_steps takes dK(n_steps - 1) only.
+  // KIND: 0 first, 1 full, 2 last.
+  auto iter_second = [&](auto slot_c, int j, auto kind_c) __attribute__((always_inline)) {
+    constexpr int SL = decltype(slot_c)::value;
+    constexpr int NX = (SL + 1) % 3, PV = (SL + 2) % 3;
+    constexpr int KIND = decltype(kind_c)::value;
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (KIND == 0)
+      chain(ic<0>{}, ic<2 * DS>{}, ic<PV>{}, ic<SL>{});
+    else if constexpr (KIND == 1)
+      chain(ic<4 * DB>{}, ic<2 * DS>{}, ic<PV>{}, ic<SL>{});
+    else
+      chain(ic<4 * DB>{}, ic<0>{}, ic<PV>{}, ic<SL>{});
+    __builtin_amdgcn_s_setprio(0);
+    // stage j+1 landed; the dS stores of step j-1 (issued after it) may not have
+    if constexpr (DS_STORES > 0 && KIND != 0)
+      phase_barrier<DS_STORES>();
+    else
+      phase_barrier<0>();
+    if (j + 2 < n_steps) issue(ic<PV>{}, j + 2);
+    if (wave == 4 && j + 1 < n_steps) scale_lse(NX);
+    if constexpr (KIND != 2) make_ds(slot_c, j);
+    bare_barrier();
+  };
+
+  if (n_steps > 0) {
+    // Stages 0 and 1 in flight; stage 0 landed and published, its LSE scaled
+    // (and published); S(0).
+    if (second) {
+      issue(ic<0>{}, 0);
+      if (n_steps > 1) issue(ic<1>{}, 1);
+    }
+    if (second && n_steps > 1) {
+      if (wave == 4 || wave == 5)
+        phase_barrier<2 * ROW_LOADS + 1>();
+      else
+        phase_barrier<2 * ROW_LOADS>();
+    } else {
+      phase_barrier<0>();
+    }
+    if (wave == 4) scale_lse(0);
+    lds_barrier();
+    if (!second) {
+      __builtin_amdgcn_s_setprio(1);
+      chain(ic<0>{}, ic<2 * DS>{}, ic<0>{}, ic<0>{});
+      __builtin_amdgcn_s_setprio(0);
+      const int full = n_steps - 1;  // iterations 0 .. n_steps - 2
+      int j = 0;
+      for (; j + 3 <= full; j += 3) {
+        iter_first(ic<0>{}, j, std::true_type{});
+        iter_first(ic<1>{}, j + 1, std::true_type{});
+        iter_first(ic<2>{}, j + 2, std::true_type{});
       }
-      f32x16_t dp[2];
-#pragma unroll
-      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
-        u32x4_t da[DS];
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) da[ds] = tile_row16<D>(tdo, 32 * rb + r32, half * DS + ds);
-        __builtin_amdgcn_sched_barrier(0);
-        dp[rb] = (f32x16_t){};
-#pragma unroll
-        for (int ds = 0; ds < DS; ++ds) dp[rb] = mfma32x32x16<DT>(da[ds], bf[ds], dp[rb]);
+      if (j < full) iter_first(ic<0>{}, j++, std::true_type{});
+      if (j < full) iter_first(ic<1>{}, j++, std::true_type{});
+      // j == n_steps - 1: dV only
+      if (j % 3 == 0)
+        iter_first(ic<0>{}, j, std::false_type{});
+      else if (j % 3 == 1)
+        iter_first(ic<1>{}, j, std::false_type{});
+      else
+        iter_first(ic<2>{}, j, std::false_type{});
+      // j == n_steps: the second role finishes dK
+      phase_barrier<0>();
+      bare_barrier();
+    } else {
+      iter_second(ic<0>{}, 0, ic<0>{});
+      int j = 1;
+      for (; j + 3 <= n_steps; j += 3) {
+        iter_second(ic<1>{}, j, ic<1>{});
+        iter_second(ic<2>{}, j + 1, ic<1>{});
+        iter_second(ic<0>{}, j + 2, ic<1>{});
       }
-      lds_exchange_barrier();
-#pragma unroll
-      for (int rb = 0; rb < kBwdQT / 32; ++rb) {
-        u32x4_t tb[2 * DB];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) tb[ks * DB + db] = tile_tr<D>(tq, 2 * rb + ks, db, lane);
-        float dsv[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int lr = 32 * rb + 8 * gq + 4 * half;
-          const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(sdl + lr);
-          const f32x4_t p4 = *xchg_at(rb, gq);
-#pragma unroll
-          for (int x = 0; x < 4; ++x) dsv[4 * gq + x] = p4[x] * (dp[rb][4 * gq + x] - d4[x]);
-        }
-        u32x4_t sf[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          sf[ks] = (u32x4_t){pack2<DT>(dsv[8 * ks + 0], dsv[8 * ks + 1]),
-                             pack2<DT>(dsv[8 * ks + 2], dsv[8 * ks + 3]),
-                             pack2<DT>(dsv[8 * ks + 4], dsv[8 * ks + 5]),
-                             pack2<DT>(dsv[8 * ks + 6], dsv[8 * ks + 7])};
-        if constexpr (STORE_DS) {
-          // sf[ks] holds rows 32rb + 16ks + 8j + 4half + 0..3 in words 2j, 2j+1.
-          // Swapping the j = 1 pieces of the low half with the j = 0 pieces of
-          // the high half leaves rows 32rb + 16ks + 8half + 0..7 in each lane:
-          // one 16-byte store.
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            const auto w0 = __builtin_amdgcn_permlane32_swap(sf[ks][0], sf[ks][2], false, false);
-            const auto w1 = __builtin_amdgcn_permlane32_swap(sf[ks][1], sf[ks][3], false, false);
-            __builtin_amdgcn_raw_buffer_store_b128((u32x4_t){w0[0], w1[0], w0[1], w1[1]}, rds,
-                                                   ds_lane + (uint32_t)(32 * rb + 16 * ks) * 2u,
-                                                   0, 0);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int db = 0; db < DB; ++db) acc[db] = mfma32x32x16<DT>(tb[ks * DB + db], sf[ks], acc[db]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    for (int i = 0; i < n_steps; i += 2) {
-      if constexpr (STORE_DS) begin_step_st(i); else begin_step(i);
-      step(std::integral_constant<int, 0>{}, i);
-      if (i + 1 < n_steps) {
-        if constexpr (STORE_DS) begin_step_st(i + 1); else begin_step(i + 1);
-        step(std::integral_constant<int, 1>{}, i + 1);
-      }
+      if (j < n_steps) iter_second(ic<1>{}, j++, ic<1>{});
+      if (j < n_steps) iter_second(ic<2>{}, j++, ic<1>{});
+      // j == n_steps: dK only
+      if (j % 3 == 0)
+        iter_second(ic<0>{}, j, ic<2>{});
+      else if (j % 3 == 1)
+        iter_second(ic<1>{}, j, ic<2>{});
+      else
+        iter_second(ic<2>{}, j, ic<2>{});
     }
   }
 
