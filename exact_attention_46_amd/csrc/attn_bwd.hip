@@ -696,6 +696,31 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   int kv_end = Nk;
   if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kBwdRowsWG, Nq) - 1 + off + 1));
   const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
+  // Per-lane LDS byte addresses of the operand reads (as in the dK/dV
+  // kernel): K / V rows r32 (+32 kb) at logical chunk half*DS + ds, and the
+  // transposed K reads of tile_tr (rows 4half + kk, +8; column block db). The
+  // buffer, the tile (K or V), the row block and the k-step add compile-time
+  // offsets below 64 KiB; the empty asm keeps the compiler from folding them
+  // into the addresses.
+  uint32_t row_a[DS], tr_a[DB][2];
+  {
+    const uint32_t base = lds_addr(smem);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      row_a[ds] = base + (uint32_t)(r32 * ROW + (((half * DS + ds) ^ bwd_swz<D>(r32)) << 4));
+      asm volatile("" : "+v"(row_a[ds]));
+    }
+    const int kk = (lane & 15) >> 2, a4 = lane & 3;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int r = 4 * half + kk + 8 * w;
+        const int col = 32 * db + 16 * ((lane >> 4) & 1) + 4 * a4;
+        tr_a[db][w] = base + (uint32_t)(r * ROW + (((col >> 3) ^ bwd_swz<D>(r)) << 4) + (col & 7) * 2);
+        asm volatile("" : "+v"(tr_a[db][w]));
+      }
+  }
   auto issue = [&](int t) {
     unsigned char* st = smem + (t & 1) * STAGE;
     stage_rows<D, kBwdKT, kBwdWaves>(k + kvoff, t * kBwdKT, Nk, st, tid);
@@ -713,25 +738,48 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const unsigned char* tk = smem + BUF * STAGE;
     const unsigned char* tv = tk + TILE;
 
-    // S^T = K Q^T and dP^T = V dO^T: 64 keys x 32 rows in two 32-key blocks.
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = (f32x16_t){};
-      dp[kb] = (f32x16_t){};
-#pragma unroll
-      for (int ds = 0; ds < DS; ++ds) {
-        s[kb] = mfma32x32x16<DT>(tile_row16<D>(tk, 32 * kb + r32, half * DS + ds), qf[ds], s[kb]);
-        dp[kb] = mfma32x32x16<DT>(tile_row16<D>(tv, 32 * kb + r32, half * DS + ds), dof[ds], dp[kb]);
+    // Per 32-key block kb, one sequence of products: S^T = K Q^T (DS
+    // products into s) and dP^T = V dO^T (DS into dp), then dS^T from them,
+    // then dQ^T += K^T dS^T for the block's two 16-key steps (2 DB products).
+    // A operands are read RA products ahead through one ring, across the dS
+    // arithmetic and into the next block, so no product waits for its own read.
+    constexpr int PB = 2 * DS + 2 * DB;  // products per block
+    constexpr int RA = 4;
+    u32x4_t ring[RA];
+    auto read_a = [&](int n) __attribute__((always_inline)) {
+      const int kb = n / PB, q = n % PB;
+      if (q < 2 * DS) {
+        const uint32_t o = BUF * STAGE + (q < DS ? 0 : TILE) + 32 * kb * ROW;
+        ring[n % RA] = lds_read16_staged(lds_ptr<const lds_u32x4_t>(row_a[q % DS] + o));
+      } else {
+        const int m = q - 2 * DS;
+        const uint32_t o = BUF * STAGE + 16 * (2 * kb + m / DB) * ROW;
+        const u32x2_t lo = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[m % DB][0] + o));
+        const u32x2_t hi = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[m % DB][1] + o));
+        ring[n % RA] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
       }
-    }
-    // dS^T, packed as the B operand of dQ^T += K^T dS^T (4 steps of 16 keys).
-    u32x4_t sf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    };
+    f32x16_t s_, dp_;
+    u32x4_t sf[2];
+    // Product n of the tile (block n / PB, index q = n % PB in the block).
+    auto product = [&](int n) __attribute__((always_inline)) {
+      const int q = n % PB;
+      if (q < DS) {
+        s_ = mfma32x32x16<DT>(ring[n % RA], qf[q], q == 0 ? (f32x16_t){} : s_);
+      } else if (q < 2 * DS) {
+        dp_ = mfma32x32x16<DT>(ring[n % RA], dof[q - DS], q == DS ? (f32x16_t){} : dp_);
+      } else {
+        const int m = q - 2 * DS;
+        dqa[m % DB] = mfma32x32x16<DT>(ring[n % RA], sf[m / DB], dqa[m % DB]);
+      }
+      if (n + RA < 2 * PB) read_a(n + RA);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // dS^T of block kb, packed as the B operand of its two dQ steps.
+    auto make_ds = [&](int kb) __attribute__((always_inline)) {
       float x[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = fast_exp2(__builtin_fmaf(s[kb][e], c, -l2));
+      for (int e = 0; e < 16; ++e) x[e] = fast_exp2(__builtin_fmaf(s_[e], c, -l2));
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -741,17 +789,26 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = x[e] * (dp[kb][e] - dl);
+      for (int e = 0; e < 16; ++e) x[e] = x[e] * (dp_[e] - dl);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        sf[2 * kb + j] = (u32x4_t){pack2<DT>(x[8 * j + 0], x[8 * j + 1]), pack2<DT>(x[8 * j + 2], x[8 * j + 3]),
-                                   pack2<DT>(x[8 * j + 4], x[8 * j + 5]), pack2<DT>(x[8 * j + 6], x[8 * j + 7])};
-    }
+        sf[j] = (u32x4_t){pack2<DT>(x[8 * j + 0], x[8 * j + 1]), pack2<DT>(x[8 * j + 2], x[8 * j + 3]),
+                          pack2<DT>(x[8 * j + 4], x[8 * j + 5]), pack2<DT>(x[8 * j + 6], x[8 * j + 7])};
+      __builtin_amdgcn_sched_barrier(0);
+    };
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int n = 0; n < RA; ++n) read_a(n);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqa[db] = mfma32x32x16<DT>(tile_tr<D>(tk, ks, db, lane), sf[ks], dqa[db]);
+    for (int q = 0; q < 2 * DS; ++q) product(q);
+    make_ds(0);
+#pragma unroll
+    for (int q = 2 * DS; q < PB; ++q) product(q);
+#pragma unroll
+    for (int q = 0; q < 2 * DS; ++q) product(PB + q);
+    make_ds(1);
+#pragma unroll
+    for (int q = 2 * DS; q < PB; ++q) product(PB + q);
   };
   // Start of tile t: its loads (this wave's) have landed; the barrier
   // publishes the rest and ends all reads of tile t-1, whose buffer tile t+1
