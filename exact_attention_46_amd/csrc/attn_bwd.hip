@@ -49,6 +49,21 @@
 
 namespace mi355attn {
 
+typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
+
+// An LDS pointer from a 32-bit LDS byte address.
+template <typename T>
+__device__ __forceinline__ T* lds_ptr(uint32_t addr) {
+  return (T*)(size_t)addr;
+}
+
+// 16-byte LDS read of a tile staged with buffer loads to LDS (restrict-scoped
+// for the same reason as lds_read_tr16_staged: no wait for the loads still in
+// flight, which write other bytes).
+__device__ __forceinline__ u32x4_t lds_read16_staged(const lds_u32x4_t* __restrict__ p) {
+  return *p;
+}
+
 constexpr int kBwdWaves = 4;                   // dQ workgroup
 constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kDkdvWaves = 8;                  // dK/dV workgroup: 4 key blocks x 2 roles

@@ -145,20 +145,6 @@ __device__ __forceinline__ u32x2_t lds_read_tr16_staged(const lds_s16x4_t* __res
                             __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_s16x4_t*>(p)));
 }
 
-typedef __attribute__((address_space(3))) u32x4_t lds_u32x4_t;
-
-// An LDS pointer from a 32-bit LDS byte address.
-template <typename T>
-__device__ __forceinline__ T* lds_ptr(uint32_t addr) {
-  return (T*)(size_t)addr;
-}
-
-// 16-byte LDS read for kernels that stage tiles with buffer loads to LDS
-// (restrict-scoped for the same reason as lds_read_tr16_staged).
-__device__ __forceinline__ u32x4_t lds_read16_staged(const lds_u32x4_t* __restrict__ p) {
-  return *p;
-}
-
 // 32-bit LDS byte address of a pointer into __shared__ memory.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
