@@ -700,6 +700,55 @@ def test_backward(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     _check_grad(outs[2][1], rv, bv, dtype, tag + " dv")
 
 
+def _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    """attn_bwd and attn_bwd_ds on one case, each against the oracle with the
+    per-element gradient bound."""
+    seed = zlib.crc32(repr(("bwd-steps", B, Hq, Hkv, Nq, Nk, d, dtype, causal)).encode()) % 10000
+    q, k, v = wl.prefill_inputs(B, Hq, Hkv, Nq, Nk, d, dtype, seed)
+    g = torch.Generator().manual_seed(seed + 1)
+    do = torch.randn(q.shape, generator=g).to(q.dtype)
+    scale = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = ea.fwd(qd, kd, vd, causal=causal, scale=scale)
+    rq, rk, rv = oracle.attn_bwd(wl.bits(q), wl.bits(k), wl.bits(v), wl.bits(do),
+                                 wl.DTYPE_CODE[dtype], scale, causal)
+    bq, bk, bv = grad_bound(q, k, v, do, dtype, scale, causal)
+    for form in ("bwd", "bwd_ds"):
+        outs = [_guarded(t.shape, t.dtype) for t in (qd, kd, vd)]
+        deltab, delta = _guarded(tuple(lse.shape), torch.float32)
+        if form == "bwd":
+            ea.attn_bwd(qd, kd, vd, o, dod, lse, delta, outs[0][1], outs[1][1], outs[2][1],
+                        causal, scale)
+        else:
+            ds = torch.full((ea.attn_bwd_ds_workspace(B, Hq, Nq, Nk),), 0xFF, dtype=torch.uint8,
+                            device="cuda")
+            ea.attn_bwd_ds(qd, kd, vd, o, dod, lse, delta, ds, outs[0][1], outs[1][1],
+                           outs[2][1], causal, scale)
+        torch.cuda.synchronize()
+        for buf, t in outs + [(deltab, delta)]:
+            assert _guard_ok(buf, t.numel()), "write outside an output"
+        tag = "%s %s" % (form, (B, Hq, Hkv, Nq, Nk, d, dtype, causal))
+        _check_grad(outs[0][1], rq, bq, dtype, tag + " dq")
+        _check_grad(outs[1][1], rk, bk, dtype, tag + " dk")
+        _check_grad(outs[2][1], rv, bv, dtype, tag + " dv")
+
+
+# The dK/dV kernel walks 64-row steps (every query head of a GQA group) in a
+# three-slot ring, with its first and last iterations compiled apart from the
+# steady-state loop: non-causal cases with Nq = 64 n and one 128-key block give
+# every workgroup exactly n (or group * n) steps, so these cover each step count
+# from 1 to 8 and each slot the loop can end on, for both roles.
+BWD_STEPS = ([(1, 2, 2, 64 * n, 128, 128, "bf16", False) for n in range(1, 8)] +
+             [(1, 4, 2, 64 * n, 96, 64, "fp16", False) for n in (1, 2, 3, 4)] +
+             [(1, 2, 2, 64 * 5 - 17, 128, 128, "bf16", False),
+              (2, 2, 1, 64 * 3, 128, 64, "bf16", True)])
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", BWD_STEPS)
+def test_backward_step_counts(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal)
+
+
 def test_backward_full_size_sampled_heads():
     """The backward on the whole llm_prefill workload, in the launch configuration
     the benchmark times; three (batch, head) slices, first and last included, are
