@@ -741,7 +741,11 @@ def _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
 BWD_STEPS = ([(1, 2, 2, 64 * n, 128, 128, "bf16", False) for n in range(1, 8)] +
              [(1, 4, 2, 64 * n, 96, 64, "fp16", False) for n in (1, 2, 3, 4)] +
              [(1, 2, 2, 64 * 5 - 17, 128, 128, "bf16", False),
-              (2, 2, 1, 64 * 3, 128, 64, "bf16", True)])
+              (2, 2, 1, 64 * 3, 128, 64, "bf16", True),
+              # one row and one key; a short causal block against a long key range
+              # (workgroups whose keys no row sees take no step at all)
+              (1, 2, 2, 1, 1, 128, "bf16", True),
+              (1, 2, 1, 17, 300, 64, "fp16", True)])
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", BWD_STEPS)
