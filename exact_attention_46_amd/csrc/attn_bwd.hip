@@ -17,27 +17,25 @@
 //    second keeps their V rows, computes dP = dO V^T, takes P from the first
 //    through LDS, forms dS = P (dP - D) and accumulates dK^T += Q^T dS (32x32x16
 //    MFMA, fp32 accumulate). Each wave holds one operand block and one
-//    accumulator, so it fits in 256 registers and two waves share each SIMD,
-//    one running element-wise work or waiting on LDS while the other issues
-//    products. The workgroup walks 64-row tiles of Q and dO (every query head of
-//    the group) staged in LDS with their LSE and D, two buffers deep: the next
-//    tile's loads go out right after the barrier that publishes the current
-//    one and land while the current one is computed. The S / dP accumulators
-//    hold one key per lane and 16 rows per lane, which is the B-operand layout
-//    of the next products, so P and dS enter them as they are (rounded to the
-//    input dtype), with dO^T and Q^T read from the staged tiles by transposing
-//    LDS reads.
+//    accumulator, so it fits in 256 registers and two waves share each SIMD.
+//    The workgroup walks 64-row steps of Q and dO (every query head of the
+//    group), staged in LDS with their LSE and D in a three-slot ring, in two
+//    phases per step in which the two waves of a SIMD take opposite roles: one
+//    issues products while the other forms P or dS (the schedule is described
+//    at the kernel). The S / dP accumulators hold one key per lane and 16 rows
+//    per lane, which is the B-operand layout of the next products, so P and dS
+//    enter them as they are (rounded to the input dtype), with dO^T and Q^T
+//    read from the staged tiles by transposing LDS reads.
 //  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (batch, head);
 //    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
-//    of K and V staged in LDS (two buffers deep, as above): S^T = K Q^T,
+//    of K and V staged in LDS (two buffers deep: the next tile's loads go out
+//    right after the barrier that publishes the current one): S^T = K Q^T,
 //    dP^T = V dO^T (one query row per lane), dS^T, then dQ^T += K^T dS^T with
-//    K^T from transposing reads. It runs first and also computes D for its
-//    rows (from their dO and O rows, each lane pair summing half of d), which
-//    the dK/dV kernel then reads. Its operands are read as the products need
-//    them, which keeps a wave within 256 registers: two workgroups share a CU
-//    (128 KiB of LDS), so each SIMD switches between two waves while one waits
-//    on LDS or its barrier (0.69 -> 0.42 ms at B=4, H=32, N=2048, d=128, causal,
-//    against one wave per SIMD with all operands read ahead in batches).
+//    K^T from transposing reads, per 32-key block, with every A operand read
+//    four products ahead. It runs first and also computes D for its rows (from
+//    their dO and O rows, each lane pair summing half of d), which the dK/dV
+//    kernel then reads. Two workgroups share a CU (128 KiB of LDS), two waves
+//    per SIMD.
 // The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
 // instead of 5), which is what removes the atomics on dQ.
 #include <type_traits>
