@@ -639,8 +639,52 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- dQ
 
+// dQ: one workgroup of 8 waves per 256 query rows of one (batch, head). Each
+// wave keeps its 32 rows of Q^T and dO^T in registers as B operands and walks
+// the 32-key blocks of the workgroup's key range: S^T = K Q^T and dP^T = V dO^T
+// (one query row per lane, so LSE and D are per-lane scalars), dS^T, then
+// dQ^T += K^T dS^T with K^T from transposing reads. The two waves of a SIMD
+// (w and w + 4, owning adjacent 32-row blocks) alternate in phases separated by
+// workgroup barriers: in its matrix phase for block j a wave issues dQ(j - 1),
+// S(j) and dP(j) (24 products at d = 128) while its partner forms dS of its own
+// block on the vector ALU; the second wave runs one phase behind the first.
+//
+//   phase   first wave (rows 64p .. 64p+31)    second wave (rows 64p+32 ..)
+//   0       S(0), dP(0)                          -
+//   2j+1    dS(j)                                dQ(j-1), S(j), dP(j)
+//   2j+2    dQ(j), S(j+1), dP(j+1)               dS(j)
+//
+// 64-key tiles of K and V are staged in LDS three slots deep by the second
+// waves: tile t + 3 goes into the slot of tile t in the phase after the second
+// waves' dQ(2t + 1) (the slot's last reader), six phases before its first use,
+// and each second wave waits for its share of a tile, with a counted vmcnt, at
+// the barrier before the phase that first reads it.
+constexpr int kDqWaves = 8;
+constexpr int kDqThreads = 64 * kDqWaves;
+constexpr int kDqRowsWG = 32 * kDqWaves;
+constexpr int kDqSlots = 3;
+
+// Workgroup L's (unit, rank) of the dQ kernel: as bwd_block_of, each XCD is
+// given a contiguous range of units, but walks it kDqL2Units units at a time
+// with the row blocks of those units in rank order across them (the heaviest
+// causal blocks of all of them first), so that the list the dispatcher deals
+// out to the XCD's CUs goes from heavy to light within each group instead of
+// within each unit (the K and V of the group's units fit in the XCD's L2).
+constexpr int kDqL2Units = 4;
+__device__ __forceinline__ void dq_block_of(int L, int units, int per_unit, int& unit, int& rank) {
+  constexpr int G = kDqL2Units;
+  if (units % 8 == 0 && (units / 8) % G == 0) {
+    const int x = L % 8, s = L / 8;
+    const int grp = s / (G * per_unit), r = s % (G * per_unit);
+    unit = x * (units / 8) + grp * G + r % G;
+    rank = r / G;
+  } else {
+    bwd_block_of(L, units, per_unit, unit, rank);
+  }
+}
+
 template <int DT, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdThreads, 2)
+__global__ void __launch_bounds__(kDqThreads, 1)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
                    const uint16_t* __restrict__ dout, const float* __restrict__ lse,
@@ -648,80 +692,122 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                    int Nq, int Nk, float scale) {
   constexpr int DS = D / 16, DB = D / 32, ROW = D * 2;
   constexpr int TILE = kBwdKT * ROW;
-  constexpr int STAGE = 2 * TILE;  // K, V
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int V_AT = kDqSlots * TILE;      // K slots, then V slots
+  constexpr int STG_AT = 2 * kDqSlots * TILE;  // then each wave's 32-row staging slot
+  constexpr int STG = 32 * ROW;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[STG_AT + kDqWaves * STG];
+  static_assert(STG_AT + kDqWaves * STG <= 160 * 1024, "LDS of a gfx950 workgroup");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool second = wave >= kDqWaves / 2;
   const int r32 = lane & 31, half = lane >> 5;
-  const int nqt = (Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  const int nqt = (Nq + kDqRowsWG - 1) / kDqRowsWG;
   // b * Hq + h and its row block; the causally heaviest (last) blocks of a
   // unit go first.
   int unit, qt;
-  bwd_block_of(blockIdx.x, B * Hq, nqt, unit, qt);
+  dq_block_of(blockIdx.x, B * Hq, nqt, unit, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int b = unit / Hq, h = unit % Hq;
   const int g = h / (Hq / Hkv);
   const int off = Nk - Nq;
-  const int q0 = qt * kBwdRowsWG;
-  const int qw0 = q0 + 32 * wave;
+  const int q0 = qt * kDqRowsWG;
+  const int qw0 = q0 + 32 * (2 * (wave & 3) + (second ? 1 : 0));
   const int my_row = qw0 + r32;  // this lane's query row (column of S^T)
   const int64_t qrow0 = ((int64_t)b * Hq + h) * (int64_t)Nq;
   const int64_t kvoff = ((int64_t)b * Hkv + g) * (int64_t)Nk * D;
 
-  // Q^T and dO^T B operands: lane row r32, chunk half*DS + ds (rows >= Nq zero).
-  u32x4_t qf[DS], dof[DS];
-  {
-    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)));
-    const auto rq = make_rsrc(q + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
-    const auto rd = make_rsrc(dout + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
-#pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
-      const uint32_t o16 = (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4);
-      qf[ds] = buf_load16(rq, o16);
-      dof[ds] = buf_load16(rd, o16);
-    }
-  }
+  // Keys the workgroup's rows may see: [0, kv_end); tiles of 64 keys, blocks
+  // of 32. This wave's rows see blocks [0, nb).
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kDqRowsWG, Nq) - 1 + off + 1));
+  const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
+  const int n_blocks = 2 * n_tiles;
+  int w_end = qw0 < Nq ? Nk : 0;
+  if (CAUSAL && qw0 < Nq) w_end = max(0, min(Nk, min(qw0 + 32, Nq) - 1 + off + 1));
+  const int nb = __builtin_amdgcn_readfirstlane((w_end + 31) / 32);
+
+  // Tile t of K and V into slot t % 3, issued by the second waves (each moves
+  // TILE_LOADS KiB of it).
+  constexpr int TILE_LOADS = 2 * (kBwdKT / (64 / (D / 8))) / (kDqWaves / 2);
+  auto issue = [&](int t) {
+    const int rtid = tid - 64 * (kDqWaves / 2);
+    unsigned char* kt = smem + (t % kDqSlots) * TILE;
+    stage_rows<D, kBwdKT, kDqWaves / 2>(k + kvoff, t * kBwdKT, Nk, kt, rtid);
+    stage_rows<D, kBwdKT, kDqWaves / 2>(v + kvoff, t * kBwdKT, Nk, kt + V_AT, rtid);
+  };
   const bool row_ok = my_row < Nq;
-  const float l2 = row_ok ? lse[qrow0 + my_row] * kLog2e : 0.f;
+
+  // Q^T and dO^T B operands (lane row r32, chunk half*DS + ds; rows >= Nq
+  // zero) and D of the wave's rows. The rows go through LDS: whole 1 KiB row
+  // runs per load into the wave's staging slot (Q) and, before any tile is
+  // staged, into the tile area (dO), then into registers by conflict-free
+  // swizzled reads; O follows into the Q slot. (Loading the operand layout
+  // straight from memory makes every load touch 32 rows.)
+  const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)));
+  unsigned char* stg_q = smem + STG_AT + wave * STG;
+  unsigned char* stg_d = smem + wave * STG;
+  stage_rows<D, 32, 1>(q + (qrow0 + qw0) * D, 0, valid, stg_q, lane);
+  stage_rows<D, 32, 1>(dout + (qrow0 + qw0) * D, 0, valid, stg_d, lane);
+  const float lse_row = row_ok ? lse[qrow0 + my_row] : 0.f;
+  const int s_off = r32 * ROW;
+  u32x4_t qf[DS], dof[DS];
+  wait_vmcnt<0>();
+  const float l2 = lse_row * kLog2e;
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds) {
+    const int c16 = ((half * DS + ds) ^ bwd_swz<D>(r32)) << 4;
+    qf[ds] = *reinterpret_cast<const u32x4_t*>(stg_q + s_off + c16);
+    dof[ds] = *reinterpret_cast<const u32x4_t*>(stg_d + s_off + c16);
+  }
+  wait_lgkmcnt0();
+  stage_rows<D, 32, 1>(o + (qrow0 + qw0) * D, 0, valid, stg_q, lane);
+  // Every wave has read its dO rows out of the tile area.
+  bare_barrier();
+  if (second && n_tiles > 0) issue(0);
+  // O has landed (tile 0, issued after it, may not have).
+  if (second && n_tiles > 0)
+    wait_vmcnt<TILE_LOADS>();
+  else
+    wait_vmcnt<0>();
   // D of this lane's row, sum_t dO_t O_t: each lane of the pair (l, l ^ 32)
   // sums its half of d; the first-half lane stores D for the dK/dV kernel.
   float dl;
   {
-    const int valid = __builtin_amdgcn_readfirstlane(max(0, min(32, Nq - qw0)));
-    const auto ro = make_rsrc(o + (qrow0 + qw0) * D, (uint32_t)valid * ROW);
     float acc = 0.f;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const u32x4_t ov = buf_load16(ro, (uint32_t)r32 * ROW + (uint32_t)((half * DS + ds) << 4));
+      const u32x4_t ov = *reinterpret_cast<const u32x4_t*>(
+          stg_q + s_off + (((half * DS + ds) ^ bwd_swz<D>(r32)) << 4));
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = dot2_acc<DT>(ov[j], dof[ds][j], acc);
     }
     dl = sum_with_partner32(acc);
     if (row_ok && half == 0) delta[qrow0 + my_row] = dl;
   }
+  if (second && n_tiles > 1) issue(1);
   const float c = scale * kLog2e;
   f32x16_t dqa[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) dqa[db] = (f32x16_t){};
 
-  // Keys the workgroup's rows may see: [0, kv_end).
-  int kv_end = Nk;
-  if (CAUSAL) kv_end = max(0, min(Nk, min(q0 + kBwdRowsWG, Nq) - 1 + off + 1));
-  const int n_tiles = (kv_end + kBwdKT - 1) / kBwdKT;
   // Per-lane LDS byte addresses of the operand reads (as in the dK/dV
-  // kernel): K / V rows r32 (+32 kb) at logical chunk half*DS + ds, and the
+  // kernel): K rows and V rows r32 at logical chunk half*DS + ds (two
+  // families: the V slots lie beyond the 64 KiB reach of one base), and the
   // transposed K reads of tile_tr (rows 4half + kk, +8; column block db). The
-  // buffer, the tile (K or V), the row block and the k-step add compile-time
-  // offsets below 64 KiB; the empty asm keeps the compiler from folding them
-  // into the addresses.
-  uint32_t row_a[DS], tr_a[DB][2];
+  // slot, the 32-key half and the k-step add compile-time offsets below
+  // 64 KiB; the empty asm keeps the compiler from folding them into the
+  // addresses.
+  uint32_t row_k[DS], row_v[DS], tr_a[DB][2];
   {
     const uint32_t base = lds_addr(smem);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      row_a[ds] = base + (uint32_t)(r32 * ROW + (((half * DS + ds) ^ bwd_swz<D>(r32)) << 4));
-      asm volatile("" : "+v"(row_a[ds]));
+      const uint32_t a = base + (uint32_t)(r32 * ROW + (((half * DS + ds) ^ bwd_swz<D>(r32)) << 4));
+      row_k[ds] = a;
+      row_v[ds] = a + V_AT;
+      asm volatile("" : "+v"(row_k[ds]));
+      asm volatile("" : "+v"(row_v[ds]));
     }
     const int kk = (lane & 15) >> 2, a4 = lane & 3;
 #pragma unroll
@@ -734,111 +820,191 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         asm volatile("" : "+v"(tr_a[db][w]));
       }
   }
-  auto issue = [&](int t) {
-    unsigned char* st = smem + (t & 1) * STAGE;
-    stage_rows<D, kBwdKT, kBwdWaves>(k + kvoff, t * kBwdKT, Nk, st, tid);
-    stage_rows<D, kBwdKT, kBwdWaves>(v + kvoff, t * kBwdKT, Nk, st + TILE, tid);
-  };
-  // Each tile is compiled for both stage buffers (every LDS address a per-lane
-  // base set up once plus an immediate offset); masking only where a tile
-  // straddles this wave's diagonal or a ragged edge, and no products for a
-  // tile wholly above the diagonal.
-  auto step = [&](auto buf_c, int t) {
-    constexpr int BUF = decltype(buf_c)::value;
-    const int k0 = t * kBwdKT;
-    if (CAUSAL && k0 > qw0 + 31 + off) return;
-    const bool masked = qw0 + 32 > Nq || k0 + kBwdKT > Nk || (CAUSAL && k0 + kBwdKT - 1 > qw0 + off);
-    const unsigned char* tk = smem + BUF * STAGE;
-    const unsigned char* tv = tk + TILE;
 
-    // Per 32-key block kb, one sequence of products: S^T = K Q^T (DS
-    // products into s) and dP^T = V dO^T (DS into dp), then dS^T from them,
-    // then dQ^T += K^T dS^T for the block's two 16-key steps (2 DB products).
-    // A operands are read RA products ahead through one ring, across the dS
-    // arithmetic and into the next block, so no product waits for its own read.
-    constexpr int PB = 2 * DS + 2 * DB;  // products per block
-    constexpr int RA = 4;
-    u32x4_t ring[RA];
+  f32x16_t s_, dp_;  // S^T and dP^T of the block between its two phases
+  u32x4_t sf[2];     // dS^T of the block, B operands of its two dQ steps
+  // Matrix phase: dQ^T += K^T dS^T of block RQ (when HQ; chained per
+  // accumulator: product n is d-block n / 2, 16-key step n % 2), then
+  // S^T = K Q^T and dP^T = V dO^T of block RS (when HS). Block j is 32-key half
+  // j % 2 of tile j / 2 in slot (j / 2) % 3, so R = j % 6 fixes every LDS
+  // offset. A operands are read RA products ahead through one ring; with PRE
+  // the first RA reads (dQ operands of a block staged long before) were issued
+  // during the wave's preceding vector phase.
+  constexpr int RA = 4;
+  static_assert(2 * DB >= RA, "prefetched reads are all dQ operands");
+  u32x4_t ring[RA];
+  auto read_dq = [&](auto rq_c, int n) __attribute__((always_inline)) {
+    constexpr int RQ = decltype(rq_c)::value;
+    const uint32_t o = (RQ / 2) * TILE + 16 * (2 * (RQ % 2) + n % 2) * ROW;
+    const u32x2_t lo = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[n / 2][0] + o));
+    const u32x2_t hi = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[n / 2][1] + o));
+    ring[n % RA] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+  };
+  auto prefetch = [&](auto rq_c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int n = 0; n < RA; ++n) read_dq(rq_c, n);
+  };
+  auto mphase = [&](auto hq_c, auto hs_c, auto rq_c, auto rs_c, auto pre_c) __attribute__((always_inline)) {
+    constexpr bool HQ = decltype(hq_c)::value, HS = decltype(hs_c)::value;
+    constexpr bool PRE = decltype(pre_c)::value;
+    constexpr int RS = decltype(rs_c)::value;
+    constexpr int NQ = HQ ? 2 * DB : 0, NP = NQ + (HS ? 2 * DS : 0);
+    static_assert(!PRE || HQ, "prefetch only for dQ products");
     auto read_a = [&](int n) __attribute__((always_inline)) {
-      const int kb = n / PB, q = n % PB;
-      if (q < 2 * DS) {
-        const uint32_t o = BUF * STAGE + (q < DS ? 0 : TILE) + 32 * kb * ROW;
-        ring[n % RA] = lds_read16_staged(lds_ptr<const lds_u32x4_t>(row_a[q % DS] + o));
+      if (n < NQ) {
+        read_dq(rq_c, n);
       } else {
-        const int m = q - 2 * DS;
-        const uint32_t o = BUF * STAGE + 16 * (2 * kb + m / DB) * ROW;
-        const u32x2_t lo = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[m % DB][0] + o));
-        const u32x2_t hi = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[m % DB][1] + o));
-        ring[n % RA] = (u32x4_t){lo[0], lo[1], hi[0], hi[1]};
+        const int p = n - NQ;
+        const uint32_t o = (RS / 2) * TILE + 32 * (RS % 2) * ROW;
+        ring[n % RA] = lds_read16_staged(
+            lds_ptr<const lds_u32x4_t>((p < DS ? row_k[p % DS] : row_v[p % DS]) + o));
       }
     };
-    f32x16_t s_, dp_;
-    u32x4_t sf[2];
-    // Product n of the tile (block n / PB, index q = n % PB in the block).
     auto product = [&](int n) __attribute__((always_inline)) {
-      const int q = n % PB;
-      if (q < DS) {
-        s_ = mfma32x32x16<DT>(ring[n % RA], qf[q], q == 0 ? (f32x16_t){} : s_);
-      } else if (q < 2 * DS) {
-        dp_ = mfma32x32x16<DT>(ring[n % RA], dof[q - DS], q == DS ? (f32x16_t){} : dp_);
+      if (n < NQ) {
+        dqa[n / 2] = mfma32x32x16<DT>(ring[n % RA], sf[n % 2], dqa[n / 2]);
       } else {
-        const int m = q - 2 * DS;
-        dqa[m % DB] = mfma32x32x16<DT>(ring[n % RA], sf[m / DB], dqa[m % DB]);
+        const int p = n - NQ;
+        if (p < DS)
+          s_ = mfma32x32x16<DT>(ring[n % RA], qf[p], p == 0 ? (f32x16_t){} : s_);
+        else
+          dp_ = mfma32x32x16<DT>(ring[n % RA], dof[p - DS], p == DS ? (f32x16_t){} : dp_);
       }
-      if (n + RA < 2 * PB) read_a(n + RA);
+      if (n + RA < NP) read_a(n + RA);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // dS^T of block kb, packed as the B operand of its two dQ steps.
-    auto make_ds = [&](int kb) __attribute__((always_inline)) {
-      float x[16];
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!PRE) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = fast_exp2(__builtin_fmaf(s_[e], c, -l2));
-      if (masked) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
-          const bool ok = row_ok && key < Nk && (!CAUSAL || key <= my_row + off);
-          x[e] = ok ? x[e] : 0.f;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 16; ++e) x[e] = x[e] * (dp_[e] - dl);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        sf[j] = (u32x4_t){pack2<DT>(x[8 * j + 0], x[8 * j + 1]), pack2<DT>(x[8 * j + 2], x[8 * j + 3]),
-                          pack2<DT>(x[8 * j + 4], x[8 * j + 5]), pack2<DT>(x[8 * j + 6], x[8 * j + 7])};
-      __builtin_amdgcn_sched_barrier(0);
-    };
-#pragma unroll
-    for (int n = 0; n < RA; ++n) read_a(n);
+      for (int n = 0; n < RA && n < NP; ++n) read_a(n);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int q = 0; q < 2 * DS; ++q) product(q);
-    make_ds(0);
-#pragma unroll
-    for (int q = 2 * DS; q < PB; ++q) product(q);
-#pragma unroll
-    for (int q = 0; q < 2 * DS; ++q) product(PB + q);
-    make_ds(1);
-#pragma unroll
-    for (int q = 2 * DS; q < PB; ++q) product(PB + q);
+    for (int n = 0; n < NP; ++n) product(n);
+    __builtin_amdgcn_s_setprio(0);
   };
-  // Start of tile t: its loads (this wave's) have landed; the barrier
-  // publishes the rest and ends all reads of tile t-1, whose buffer tile t+1
-  // reuses.
-  auto begin_tile = [&](int t) {
-    wait_all_memory();
-    __syncthreads();
-    if (t + 1 < n_tiles) issue(t + 1);
-  };
-  if (n_tiles > 0) issue(0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    begin_tile(t);
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) {
-      begin_tile(t + 1);
-      step(std::integral_constant<int, 1>{}, t + 1);
+  constexpr std::true_type yes{};
+  constexpr std::false_type no{};
+  // dQ(j) alone, the wave's last matrix phase (once per wave: LDS offsets
+  // added at run time).
+  auto m_dq_any = [&](int j) __attribute__((always_inline)) {
+    const uint32_t o0 = (uint32_t)(((j / 2) % kDqSlots) * TILE + 32 * (j % 2) * ROW);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int n = 0; n < 2 * DB; ++n) {
+      const uint32_t o = o0 + 16 * (n % 2) * ROW;
+      const u32x2_t lo = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[n / 2][0] + o));
+      const u32x2_t hi = lds_read_tr16_staged(lds_ptr<const lds_s16x4_t>(tr_a[n / 2][1] + o));
+      dqa[n / 2] = mfma32x32x16<DT>((u32x4_t){lo[0], lo[1], hi[0], hi[1]}, sf[n % 2], dqa[n / 2]);
     }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // dS^T of block j from its S^T and dP^T, packed as the B operands of its
+  // two dQ steps; masked where the block straddles this wave's diagonal or a
+  // ragged edge.
+  auto vphase = [&](int j) __attribute__((always_inline)) {
+    const int k0 = 32 * j;
+    const bool masked = qw0 + 32 > Nq || k0 + 32 > Nk || (CAUSAL && k0 + 31 > qw0 + off);
+    float x[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = fast_exp2(__builtin_fmaf(s_[e], c, -l2));
+    if (masked) {
+      // Keys k0 + 8(e/4) + 4half + e%4 up to this row's last key stay.
+      const int kmax = row_ok ? (CAUSAL ? min(Nk - 1, my_row + off) : Nk - 1) : -1;
+      const int lim = kmax - (k0 + 4 * half);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) x[e] = 8 * (e >> 2) + (e & 3) <= lim ? x[e] : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) x[e] = x[e] * (dp_[e] - dl);
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      sf[u] = (u32x4_t){pack2<DT>(x[8 * u + 0], x[8 * u + 1]), pack2<DT>(x[8 * u + 2], x[8 * u + 3]),
+                        pack2<DT>(x[8 * u + 4], x[8 * u + 5]), pack2<DT>(x[8 * u + 6], x[8 * u + 7])};
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The second waves' barrier after their matrix phase of block j: for odd j
+  // it first waits for their share of tile (j + 1) / 2 (tile (j + 1) / 2 + 1,
+  // issued later, may still be in flight).
+  auto second_m_barrier = [&](int j) __attribute__((always_inline)) {
+    if (j & 1) {
+      if ((j + 1) / 2 + 1 < n_tiles)
+        phase_barrier<TILE_LOADS>();
+      else
+        phase_barrier<0>();
+    } else {
+      bare_barrier();
+    }
+  };
+
+  // Tile 0 has landed (the second waves' share; each wave's own Q, dO and O
+  // loads too); the barrier publishes it.
+  if (second && n_tiles > 1)
+    phase_barrier<TILE_LOADS>();
+  else
+    phase_barrier<0>();
+  if (n_blocks == 0) {
+    // No key for any row of the workgroup: dQ = 0, no further barrier.
+  } else if (!second) {
+    // Phases M(0) | V(j), M(j + 1) for j = 0 .. n_blocks - 1.
+    if (nb > 0) mphase(no, yes, ic<0>{}, ic<0>{}, no);
+    bare_barrier();
+    int j = 0;
+    // Steady state: M(j + 1) does dQ(j), S(j + 1), dP(j + 1); R = (j + 1) % 6.
+    auto step = [&](auto r_c) __attribute__((always_inline)) -> bool {
+      constexpr int R = decltype(r_c)::value;
+      if (j + 1 >= nb) return false;
+      prefetch(ic<(R + 5) % 6>{});
+      vphase(j);
+      bare_barrier();
+      mphase(yes, yes, ic<(R + 5) % 6>{}, r_c, yes);
+      bare_barrier();
+      ++j;
+      return true;
+    };
+    while (step(ic<1>{}) && step(ic<2>{}) && step(ic<3>{}) && step(ic<4>{}) && step(ic<5>{}) &&
+           step(ic<0>{})) {
+    }
+    for (; j < n_blocks; ++j) {
+      if (j < nb) vphase(j);
+      bare_barrier();
+      if (j == nb - 1) m_dq_any(j);
+      bare_barrier();
+    }
+  } else {
+    // Phases - | M(j), V(j) for j = 0 .. n_blocks - 1 | M(n_blocks).
+    bare_barrier();
+    if (nb > 0) mphase(no, yes, ic<0>{}, ic<0>{}, no);
+    bare_barrier();
+    if (2 < n_tiles) issue(2);
+    if (1 < nb) prefetch(ic<0>{});
+    if (nb > 0) vphase(0);
+    bare_barrier();
+    int j = 1;
+    // Steady state: M(j) does dQ(j - 1), S(j), dP(j); R = j % 6. V(j) of an
+    // even block first issues tile j / 2 + 2.
+    auto step = [&](auto r_c) __attribute__((always_inline)) -> bool {
+      constexpr int R = decltype(r_c)::value;
+      if (j >= nb) return false;
+      mphase(yes, yes, ic<(R + 5) % 6>{}, r_c, yes);
+      second_m_barrier(j);
+      if ((R & 1) == 0 && j / 2 + 2 < n_tiles) issue(j / 2 + 2);
+      if (j + 1 < nb) prefetch(r_c);
+      vphase(j);
+      bare_barrier();
+      ++j;
+      return true;
+    };
+    while (step(ic<1>{}) && step(ic<2>{}) && step(ic<3>{}) && step(ic<4>{}) && step(ic<5>{}) &&
+           step(ic<0>{})) {
+    }
+    for (; j < n_blocks; ++j) {
+      if (j == nb) m_dq_any(j - 1);
+      second_m_barrier(j);
+      if ((j & 1) == 0 && j / 2 + 2 < n_tiles) issue(j / 2 + 2);
+      bare_barrier();
+    }
+    if (nb == n_blocks) m_dq_any(n_blocks - 1);
   }
 
   // dQ = scale * (dQ^T)^T: lane row r32, d = 32db + 8(e/4) + 4half + e%4.
@@ -1063,15 +1229,15 @@ int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk) {
 template <int DT, int D, bool CAUSAL>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   // dQ first: it also writes D, which the dK/dV kernel reads.
-  const int nqt = (a.Nq + kBwdRowsWG - 1) / kBwdRowsWG;
+  const int nqt = (a.Nq + kDqRowsWG - 1) / kDqRowsWG;
   const int nkt = (a.Nk + kBwdKeysWG - 1) / kBwdKeysWG;
   MI355_LOG("attn_bwd_dq_kernel<%s,%d,%s> grid=%lld block=%d then attn_bwd_dkdv_kernel grid=%lld "
             "block=%d B=%d Hq=%d Hkv=%d Nq=%d Nk=%d scale=%g delta=%p stream=%p",
             dtype_name(DT), D, CAUSAL ? "causal" : "full", (long long)a.B * a.Hq * nqt,
-            kBwdThreads, (long long)a.B * a.Hkv * nkt, kDkdvThreads, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
+            kDqThreads, (long long)a.B * a.Hkv * nkt, kDkdvThreads, a.B, a.Hq, a.Hkv, a.Nq, a.Nk,
             (double)a.scale, (void*)a.delta, (void*)stream);
   hipLaunchKernelGGL((attn_bwd_dq_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hq * nqt)),
-                     dim3(kBwdThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     dim3(kDqThreads), 0, stream, (const uint16_t*)a.q, (const uint16_t*)a.k,
                      (const uint16_t*)a.v, (const uint16_t*)a.o, (const uint16_t*)a.dout, a.lse,
                      a.delta, (uint16_t*)a.dq, a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.scale);
   hipLaunchKernelGGL((attn_bwd_dkdv_kernel<DT, D, CAUSAL>), dim3((unsigned)(a.B * a.Hkv * nkt)),
