@@ -156,6 +156,26 @@ __device__ __forceinline__ void bwd_block_of(int L, int units, int per_unit, int
   }
 }
 
+// Workgroup L's (unit, rank) for the two recomputing gradient kernels: as
+// bwd_block_of, each XCD is given a contiguous range of units, but walks it
+// G units at a time with the blocks of those units in rank order across them
+// (every unit's causally heaviest block first), so that the list the
+// dispatcher deals out to the XCD's CUs goes from heavy to light within each
+// group instead of within each unit. The rows the group's workgroups share
+// (K and V, or Q and dO) stay in the XCD's L2.
+constexpr int kDkdvGroup = 8, kDkdvDsGroup = 2, kDqGroup = 8;
+template <int G>
+__device__ __forceinline__ void bwd_group_order(int L, int units, int per_unit, int& unit, int& rank) {
+  if (G > 1 && units % 8 == 0 && (units / 8) % G == 0) {
+    const int x = L % 8, s = L / 8;
+    const int grp = s / (G * per_unit), r = s % (G * per_unit);
+    unit = x * (units / 8) + grp * G + r % G;
+    rank = r / G;
+  } else {
+    bwd_block_of(L, units, per_unit, unit, rank);
+  }
+}
+
 // acc + a.x b.x + a.y b.y for two packed pairs of the input dtype (products exact
 // in fp32).
 template <int DT>
@@ -276,7 +296,7 @@ attn_bwd_dkdv_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict_
   // b * Hkv + g and its key block; the causally heaviest (first) blocks of a
   // unit go first.
   int unit, kt;
-  bwd_block_of(blockIdx.x, B * Hkv, nkt, unit, kt);
+  bwd_group_order<STORE_DS ? kDkdvDsGroup : kDkdvGroup>(blockIdx.x, B * Hkv, nkt, unit, kt);
   const int b = unit / Hkv, g = unit % Hkv;
   const int group = Hq / Hkv;
   const int off = Nk - Nq;  // bottom-right causal alignment
@@ -664,25 +684,6 @@ constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqRowsWG = 32 * kDqWaves;
 constexpr int kDqSlots = 3;
 
-// Workgroup L's (unit, rank) of the dQ kernel: as bwd_block_of, each XCD is
-// given a contiguous range of units, but walks it kDqL2Units units at a time
-// with the row blocks of those units in rank order across them (the heaviest
-// causal blocks of all of them first), so that the list the dispatcher deals
-// out to the XCD's CUs goes from heavy to light within each group instead of
-// within each unit (the K and V of the group's units fit in the XCD's L2).
-constexpr int kDqL2Units = 4;
-__device__ __forceinline__ void dq_block_of(int L, int units, int per_unit, int& unit, int& rank) {
-  constexpr int G = kDqL2Units;
-  if (units % 8 == 0 && (units / 8) % G == 0) {
-    const int x = L % 8, s = L / 8;
-    const int grp = s / (G * per_unit), r = s % (G * per_unit);
-    unit = x * (units / 8) + grp * G + r % G;
-    rank = r / G;
-  } else {
-    bwd_block_of(L, units, per_unit, unit, rank);
-  }
-}
-
 template <int DT, int D, bool CAUSAL>
 __global__ void __launch_bounds__(kDqThreads, 1)
 attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -706,7 +707,7 @@ attn_bwd_dq_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
   // b * Hq + h and its row block; the causally heaviest (last) blocks of a
   // unit go first.
   int unit, qt;
-  dq_block_of(blockIdx.x, B * Hq, nqt, unit, qt);
+  bwd_group_order<kDqGroup>(blockIdx.x, B * Hq, nqt, unit, qt);
   if (CAUSAL) qt = nqt - 1 - qt;
   const int b = unit / Hq, h = unit % Hq;
   const int g = h / (Hq / Hkv);
