@@ -26,16 +26,16 @@
 //    per lane, which is the B-operand layout of the next products, so P and dS
 //    enter them as they are (rounded to the input dtype), with dO^T and Q^T
 //    read from the staged tiles by transposing LDS reads.
-//  * attn_bwd_dq_kernel: one workgroup per 128 query rows of one (batch, head);
-//    each wave keeps its 32 rows of Q and dO in registers and walks 64-key tiles
-//    of K and V staged in LDS (two buffers deep: the next tile's loads go out
-//    right after the barrier that publishes the current one): S^T = K Q^T,
-//    dP^T = V dO^T (one query row per lane), dS^T, then dQ^T += K^T dS^T with
-//    K^T from transposing reads, per 32-key block, with every A operand read
-//    four products ahead. It runs first and also computes D for its rows (from
-//    their dO and O rows, each lane pair summing half of d), which the dK/dV
-//    kernel then reads. Two workgroups share a CU (128 KiB of LDS), two waves
-//    per SIMD.
+//  * attn_bwd_dq_kernel: one workgroup of 8 waves per 256 query rows of one
+//    (batch, head); each wave keeps its 32 rows of Q and dO in registers and
+//    walks the 32-key blocks of K and V staged in LDS (64-key tiles, three
+//    slots deep): S^T = K Q^T, dP^T = V dO^T (one query row per lane), dS^T,
+//    then dQ^T += K^T dS^T with K^T from transposing reads, with every A
+//    operand read four products ahead. The two waves of a SIMD alternate: one
+//    issues a block's products while the other forms its dS (the schedule is
+//    described at the kernel). It runs first and also computes D for its rows
+//    (from their dO and O rows, each lane pair summing half of d), which the
+//    dK/dV kernel then reads. One workgroup per CU, two waves per SIMD.
 // The dK/dV and dQ kernels both recompute S and dP (7 matrix products in all
 // instead of 5), which is what removes the atomics on dQ.
 #include <type_traits>
