@@ -753,6 +753,23 @@ def test_backward_step_counts(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal)
 
 
+# The dQ kernel's 256-row workgroups walk 32-key blocks of 64-key tiles staged
+# three slots deep, its two waves per SIMD one phase apart: every tile count from
+# 1 to 7 (each slot reused, the unrolled six-block loop entered and left at each
+# offset), key counts that end half-way into a tile (a last block with no key),
+# and causal blocks whose waves see different numbers of blocks (rows past the
+# keys' range see none: the workgroup takes no block at all).
+DQ_BLOCKS = ([(1, 2, 1, 256, 64 * n, 128, "bf16", False) for n in range(1, 8)] +
+             [(1, 2, 2, 256, 32 * n + 1, 64, "fp16", False) for n in (1, 4, 9)] +
+             [(1, 2, 2, 256 + 64 * n, 256 + 64 * n, 128, "bf16", True) for n in (0, 1, 3)] +
+             [(1, 4, 1, 300, 97, 128, "bf16", True), (1, 2, 2, 520, 250, 64, "bf16", True)])
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", DQ_BLOCKS)
+def test_backward_dq_block_counts(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal)
+
+
 def test_backward_full_size_sampled_heads():
     """The backward on the whole llm_prefill workload, in the launch configuration
     the benchmark times; three (batch, head) slices, first and last included, are
