@@ -62,12 +62,9 @@ __device__ __forceinline__ u32x4_t lds_read16_staged(const lds_u32x4_t* __restri
   return *p;
 }
 
-constexpr int kBwdWaves = 4;                   // dQ workgroup
-constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kDkdvWaves = 8;                  // dK/dV workgroup: 4 key blocks x 2 roles
 constexpr int kDkdvThreads = 64 * kDkdvWaves;
 constexpr int kBwdKeysWG = 32 * (kDkdvWaves / 2);  // keys per dK/dV workgroup
-constexpr int kBwdRowsWG = 32 * kBwdWaves;         // query rows per dQ workgroup
 constexpr int kBwdQT = 64;                  // query rows per dK/dV step
 constexpr int kBwdKT = 64;                  // keys per dQ step
 
@@ -234,7 +231,7 @@ using ic = std::integral_constant<int, V>;
 constexpr int kDsKeys = 64;
 constexpr int kDsRows = 128;
 constexpr int kDsBlock = kDsKeys * kDsRows * 2;
-static_assert(kDsRows == kBwdRowsWG && kDsKeys == kBwdKT && kBwdKeysWG % kDsKeys == 0 &&
+static_assert(kDsKeys == kBwdKT && kBwdKeysWG % kDsKeys == 0 &&
                   kDsRows % kBwdQT == 0,
               "a dK/dV wave's step and a dQ tile each fall in one block");
 
@@ -1226,7 +1223,7 @@ attn_bwd_dq_ds_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict
 
 int64_t bwd_grid_blocks(int B, int Hq, int Hkv, int Nq, int Nk) {
   const int64_t a = (int64_t)B * Hkv * ((Nk + kBwdKeysWG - 1) / kBwdKeysWG);
-  const int64_t c = (int64_t)B * Hq * ((Nq + kBwdRowsWG - 1) / kBwdRowsWG);
+  const int64_t c = (int64_t)B * Hq * ((Nq + kDqRowsWG - 1) / kDqRowsWG);
   return a > c ? a : c;
 }
 
