@@ -770,6 +770,19 @@ def test_backward_dq_block_counts(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
     _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal)
 
 
+# Head counts at which the gradient kernels deal their workgroups to the XCDs in
+# groups of units (a multiple of 8 units per XCD and of the group size), checked
+# whole against the oracle: every (unit, block) pair must be computed exactly once.
+BWD_GROUPED = [(1, 64, 64, 512, 512, 64, "bf16", True),
+               (1, 64, 16, 300, 300, 128, "fp16", True),
+               (2, 32, 32, 256, 256, 64, "bf16", False)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype,causal", BWD_GROUPED)
+def test_backward_grouped_order(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    _run_bwd_both(B, Hq, Hkv, Nq, Nk, d, dtype, causal)
+
+
 def test_backward_full_size_sampled_heads():
     """The backward on the whole llm_prefill workload, in the launch configuration
     the benchmark times; three (batch, head) slices, first and last included, are
