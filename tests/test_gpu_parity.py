@@ -658,6 +658,11 @@ BWD = [
     # 8 and 16 (batch, head) units: the XCD-contiguous block order of both
     # gradient kernels, with GQA and a ragged length
     (2, 8, 4, 333, 333, 128, "bf16", True),
+    # GQA 4:1 with more keys than rows (bottom-right causal alignment) and the
+    # reverse, over several 256-row dQ workgroups and 128-key dK/dV workgroups
+    (1, 16, 4, 700, 1500, 128, "fp16", True),
+    (2, 8, 2, 1100, 600, 64, "bf16", True),
+    (1, 8, 8, 1536, 1536, 64, "fp16", False),
 ]
 
 
