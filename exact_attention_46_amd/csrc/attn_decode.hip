@@ -690,7 +690,10 @@ __global__ void __launch_bounds__(256)
 attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __restrict__ part_lse,
                            const int* __restrict__ seq_lens, uint16_t* __restrict__ o,
                            float* __restrict__ lse, int B, int Hq, int C, int chunk) {
-  constexpr int PER = D / 64;  // d values per lane
+  // One wave per (b, h) row. A chunk's partial row is read by LPC lanes, 16
+  // bytes (4 d values) each, so one load instruction covers CPI chunks and U of
+  // them are in flight at once; the CPI lane groups' sums are added at the end.
+  constexpr int LPC = D / 4, CPI = 64 / LPC, U = 8;
   __shared__ float wts[4][64];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
@@ -703,6 +706,7 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
   nc = nc > C ? C : nc;
   const float* pl = part_lse + row * C;
   const float* po = part_o + row * C * D;
+  const int sub = lane / LPC, dl = (lane % LPC) * 4;
 
   // Global maximum of the chunk LSEs, lanes over chunks.
   float M = -INFINITY;
@@ -710,9 +714,7 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
 #pragma unroll
   for (int sh = 32; sh >= 1; sh >>= 1) M = fmaxf(M, __shfl_xor(M, sh, 64));
 
-  float acc[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
     for (int c0 = 0; c0 < nc; c0 += 64) {
@@ -728,34 +730,33 @@ attn_decode_combine_kernel(const float* __restrict__ part_o, const float* __rest
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
       const int n = min(64, nc - c0);
-      int j = 0;
-      for (; j + 4 <= n; j += 4) {  // four independent loads in flight
-        float x[4][PER];
+      for (int j = 0; j < n; j += CPI * U) {
+        f32x4_t x[U];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < U; ++u) {
+          const int c = j + u * CPI + sub;
+          x[u] = c < n ? *reinterpret_cast<const f32x4_t*>(po + (int64_t)(c0 + c) * D + dl)
+                       : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-          for (int i = 0; i < PER; ++i) x[u][i] = po[(int64_t)(c0 + j + u) * D + lane * PER + i];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < PER; ++i) acc[i] += wts[wv][j + u] * x[u][i];
+        for (int u = 0; u < U; ++u) {
+          const int c = j + u * CPI + sub;
+          const float wc = c < n ? wts[wv][c] : 0.f;
+          acc += wc * x[u];
+        }
       }
-      for (; j < n; ++j)
-#pragma unroll
-        for (int i = 0; i < PER; ++i)
-          acc[i] += wts[wv][j] * po[(int64_t)(c0 + j) * D + lane * PER + i];
       wait_lgkmcnt0();
       __builtin_amdgcn_wave_barrier();
     }
   }
+#pragma unroll
+  for (int sh = LPC; sh < 64; sh <<= 1)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], sh, 64);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  uint16_t* orow = o + row * D + lane * PER;
-  if constexpr (PER == 2) {
-    *reinterpret_cast<uint32_t*>(orow) = pack2<DT>(acc[0] * inv, acc[1] * inv);
-  } else {
-    const uint32_t w = pack2<DT>(acc[0] * inv, 0.f);
-    *orow = (uint16_t)(w & 0xffffu);
-  }
+  if (sub == 0)
+    *reinterpret_cast<u32x2_t*>(o + row * D + dl) =
+        (u32x2_t){pack2<DT>(acc[0] * inv, acc[1] * inv), pack2<DT>(acc[2] * inv, acc[3] * inv)};
   if (lane == 0) lse[row] = wsum > 0.f ? M + kLn2 * fast_log2(wsum) : -INFINITY;
 }
 
