@@ -217,11 +217,40 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // head g*R; their results are never written.
   const uint32_t qop = (uint32_t)((r32 < R ? r32 : 0) * ROW + half * DS * 16);
 
+  // Item order. With at most 64 sequences (one per lane) and at least eight
+  // items per wave, the full chunks of all sequences come first, in sequence
+  // order, and the last, shorter chunk of each sequence after them, longest
+  // first (ties by sequence): the waves then take the short items in the last
+  // rounds, which evens out their work (on the 64-sequence decode workload at
+  // 512-key chunks the largest per-wave tile count falls from 1.065 to 1.019
+  // times the mean, and the split kernel runs 1.7 % faster; with fewer items
+  // per wave a whole item is a large part of a wave's work either way, and
+  // this order measured 2 % slower at 2048-key chunks). Lane b holds sequence
+  // b's length, its full-chunk count and the rank of its short chunk.
+  // Otherwise every valid chunk in sequence order.
+  const bool by_size = B <= 64 && n_items >= 8 * nwaves;
+  int lane_len = 0, lane_full = 0, lane_rank = 0, n_full = 0;
+  if (by_size) {
+    lane_len = lane < B ? clamp_len(seq_lens, lane, max_len) : 0;
+    lane_full = lane_len / chunk;
+    const int rem = lane_len - lane_full * chunk;
+    for (int j = 0; j < B; ++j) {
+      const int rj = __builtin_amdgcn_readlane(rem, j);
+      lane_rank += (rj > rem || (rj == rem && j < lane)) && rj > 0 ? 1 : 0;
+    }
+    if (rem == 0) lane_rank = 64;  // no short chunk
+    int f = lane_full;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) f += __shfl_xor(f, sh, 64);
+    n_full = __builtin_amdgcn_readfirstlane(f);
+  }
+
   // Sequence cursor of this wave (wave-uniform): sequence cb, whose first
-  // chunk is valid chunk number cbase, with cn chunks and length cl_len.
+  // chunk (full chunk, when ordered by size) is number cbase of that list,
+  // with cn of them and length cl_len.
   int cb = 0;
   int cl_len = clamp_len(seq_lens, 0, max_len);
-  int cn = (cl_len + chunk - 1) / chunk;
+  int cn = by_size ? cl_len / chunk : (cl_len + chunk - 1) / chunk;
   int cbase = 0;
 
   // A work position: item, tile inside the item, and the item's geometry.
@@ -237,16 +266,27 @@ attn_decode_split_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if (item >= n_items) return false;
     const int idx = item / Hkv;
     p.g = item - idx * Hkv;
-    while (idx >= cbase + cn) {  // terminates: idx < the total number of chunks
-      cbase += cn;
-      ++cb;
-      cl_len = clamp_len(seq_lens, cb, max_len);
-      cn = (cl_len + chunk - 1) / chunk;
+    if (by_size && idx >= n_full) {
+      // the short chunk of rank idx - n_full
+      const int rk = idx - n_full;
+      const uint64_t m = __ballot(lane_rank == rk);
+      const int sb = (int)__builtin_ctzll(m);  // m != 0: rk < the number of short chunks
+      p.b = sb;
+      p.c = __builtin_amdgcn_readlane(lane_full, sb);
+      p.L = __builtin_amdgcn_readlane(lane_len, sb);
+      p.nc = p.c + 1;
+    } else {
+      while (idx >= cbase + cn) {  // terminates: idx < the number of chunks in the list
+        cbase += cn;
+        ++cb;
+        cl_len = clamp_len(seq_lens, cb, max_len);
+        cn = by_size ? cl_len / chunk : (cl_len + chunk - 1) / chunk;
+      }
+      p.b = cb;
+      p.c = idx - cbase;
+      p.L = cl_len;
+      p.nc = (cl_len + chunk - 1) / chunk;
     }
-    p.b = cb;
-    p.c = idx - cbase;
-    p.L = cl_len;
-    p.nc = cn;
     const int lo = p.c * chunk;
     const int hi = min(p.L, lo + chunk);
     p.n_tiles = (hi - lo + kSplitBN - 1) / kSplitBN;

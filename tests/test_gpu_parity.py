@@ -302,6 +302,14 @@ DECODE = [
     (64, 32, 8, 128, "bf16", None, 1024, 32),
     (64, 32, 8, 128, "bf16", None, 1024, 48),
     (64, 16, 8, 64, "fp16", None, 1024, 32),
+    # 8 840 items, at least eight per wave on a 256-CU device: the short last
+    # chunks are taken after all full ones, longest first. Lengths include 0,
+    # exact multiples of the chunk (no short chunk), a short chunk alone (8) and
+    # equal remainders (1000, 1000, 1000 and 8 all leave 8 keys).
+    (64, 32, 8, 128, "bf16", [(37 * i * i + 11 * i) % 1025 if i not in (
+        0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 24, 31) else {
+        0: 0, 1: 1024, 2: 64, 3: 1000, 4: 1000, 5: 8, 6: 40, 7: 72, 8: 1023, 9: 1000, 24: 1024,
+        31: 1024}[i] for i in range(64)], 1024, 32),
 ]
 
 
