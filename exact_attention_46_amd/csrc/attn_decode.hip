@@ -10,10 +10,14 @@
 //
 // Each wave owns whole items: it walks the items w, w + W, w + 2W, ... of the
 // list of valid items (chunk slots past the end of a sequence are not in the
-// list; item i is kv-head i % Hkv of the (i / Hkv)-th valid chunk, counting
-// the chunks of all sequences in order). Since a wave visits its items in
-// increasing order, it finds their sequences with a cursor that only moves
-// forward, reading seq_lens with scalar loads; no workspace is needed.
+// list; item i is kv-head i % Hkv of the (i / Hkv)-th chunk of the list). The
+// list holds the chunks of all sequences in order or, with at most 64
+// sequences and at least eight items per wave, their full chunks in order and
+// then each sequence's shorter last chunk, longest first (see the kernel).
+// Since a wave visits its items in increasing order, it finds the sequences of
+// its full chunks with a cursor that only moves forward, reading seq_lens with
+// scalar loads, and a short chunk by its rank among the lanes of the wave;
+// no workspace is needed.
 //
 // A wave streams its items' K and V in 32-key tiles straight from HBM into
 // its own two-stage LDS ring (buffer loads to LDS, non-temporal, zero-filled
