@@ -288,6 +288,16 @@ def test_long_context_full_size_sampled():
 
 # --------------------------------------------------------------- decode
 
+# 64 sequence lengths (max_len 1024) that give 8 840 items at 32-key chunks and
+# 8 kv-heads, at least eight per wave on a 256-CU device: the split kernel then
+# takes the full chunks first and the short last chunks after them, longest
+# first. They include 0, exact multiples of the chunk (no short chunk), a short
+# chunk alone (8) and equal remainders (1000, 1000, 1000 and 8 all leave 8 keys).
+ORDERED_LENS = [(37 * i * i + 11 * i) % 1025 for i in range(64)]
+for _i, _L in {0: 0, 1: 1024, 2: 64, 3: 1000, 4: 1000, 5: 8, 6: 40, 7: 72, 8: 1023, 9: 1000,
+               24: 1024, 31: 1024}.items():
+    ORDERED_LENS[_i] = _L
+
 DECODE = [
     # B, Hq, Hkv, d, dtype, lens, max_len, chunk
     (5, 8, 2, 128, "bf16", [1, 9, 0, 31, 16], 32, 16),
@@ -302,14 +312,8 @@ DECODE = [
     (64, 32, 8, 128, "bf16", None, 1024, 32),
     (64, 32, 8, 128, "bf16", None, 1024, 48),
     (64, 16, 8, 64, "fp16", None, 1024, 32),
-    # 8 840 items, at least eight per wave on a 256-CU device: the short last
-    # chunks are taken after all full ones, longest first. Lengths include 0,
-    # exact multiples of the chunk (no short chunk), a short chunk alone (8) and
-    # equal remainders (1000, 1000, 1000 and 8 all leave 8 keys).
-    (64, 32, 8, 128, "bf16", [(37 * i * i + 11 * i) % 1025 if i not in (
-        0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 24, 31) else {
-        0: 0, 1: 1024, 2: 64, 3: 1000, 4: 1000, 5: 8, 6: 40, 7: 72, 8: 1023, 9: 1000, 24: 1024,
-        31: 1024}[i] for i in range(64)], 1024, 32),
+    # 8 840 items, at least eight per wave on a 256-CU device (see ORDERED_LENS)
+    (64, 32, 8, 128, "bf16", ORDERED_LENS, 1024, 32),
 ]
 
 
@@ -412,6 +416,7 @@ FUSED = [
     (64, 32, 8, 128, "bf16", None, 1024, 32),                 # many one-tile items per wave
     (16, 8, 8, 128, "bf16", None, 4096, 64),                  # up to 64 chunks per pair
     (2, 8, 8, 128, "fp16", [4096, 4000], 4096, 4096),         # every sequence one chunk
+    (64, 32, 8, 128, "bf16", ORDERED_LENS, 1024, 32),         # full chunks first, then short
 ]
 
 
@@ -525,6 +530,8 @@ PAGED = [
     (2, 8, 8, 128, "fp16", [4096, 4000], 4096, 512, 4096),
     # many single-tile items per wave (see DECODE)
     (64, 32, 8, 128, "bf16", None, 1024, 32, 32),
+    # full chunks first, then the short ones (see ORDERED_LENS)
+    (64, 32, 8, 128, "bf16", ORDERED_LENS, 1024, 32, 32),
 ]
 
 
